@@ -1,0 +1,383 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle is checked against things other than itself: a pure-Python brute
+force written from a different formulation, torch's float64 CPU attention and
+logsumexp (library special cases), closed forms that follow from the softmax
+definition, invariants, merge algebra, and explicit index loops for the
+relayout.  ``test_pins_catch_planted_mistakes`` plants plausible mistakes in
+copies of the oracle and checks that at least one pin fails for each.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_sequence_bidirectional_amd import inputs
+
+TOL = 1e-12
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- brute force
+def brute_attention(q, k, v, scale):
+    """Direct softmax definition, pure Python: O_i = sum_j e^{z_ij} v_j / sum_j e^{z_ij}.
+
+    No max shift, exact-ish summation with math.fsum; only for tiny inputs
+    with moderate scores.  LSE_i = ln sum_j e^{z_ij}.
+    """
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    Dv = v.shape[3]
+    O = np.zeros((B, H, Sq, Dv))
+    L = np.zeros((B, H, Sq))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Sq):
+                w = []
+                for j in range(Skv):
+                    z = scale * math.fsum(float(q[b, h, i, d]) * float(k[b, h, j, d]) for d in range(D))
+                    w.append(math.exp(z))
+                den = math.fsum(w)
+                L[b, h, i] = math.log(den)
+                for d in range(Dv):
+                    O[b, h, i, d] = math.fsum(w[j] * float(v[b, h, j, d]) for j in range(Skv)) / den
+    return O, L
+
+
+# -------------------------------------------------- pin checks (reusable)
+def pin_brute_force(attn):
+    for (B, H, Sq, Skv, D, seed) in [(1, 1, 5, 7, 4, 1), (2, 2, 9, 16, 8, 2), (1, 3, 16, 11, 8, 3)]:
+        q, k, v = rnd((B, H, Sq, D), seed), rnd((B, H, Skv, D), seed + 10), rnd((B, H, Skv, D), seed + 20)
+        scale = 1.0 / math.sqrt(D)
+        O, L = attn(q, k, v, scale)
+        Ob, Lb = brute_attention(q, k, v, scale)
+        np.testing.assert_allclose(O, Ob, rtol=0, atol=TOL)
+        np.testing.assert_allclose(L, Lb, rtol=0, atol=TOL)
+
+
+def pin_library_sdpa(attn):
+    # torch float64 CPU attention and logsumexp as an independent library route.
+    for (B, H, Sq, Skv, D, seed) in [(1, 2, 64, 48, 16, 5), (1, 1, 130, 257, 64, 6)]:
+        q, k, v = rnd((B, H, Sq, D), seed), rnd((B, H, Skv, D), seed + 1), rnd((B, H, Skv, D), seed + 2)
+        scale = 0.37
+        O, L = attn(q, k, v, scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        Ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale).numpy()
+        Lt = torch.logsumexp(scale * (tq @ tk.transpose(-1, -2)), dim=-1).numpy()
+        np.testing.assert_allclose(O, Ot, rtol=0, atol=TOL)
+        np.testing.assert_allclose(L, Lt, rtol=0, atol=TOL)
+
+
+def pin_closed_forms(attn):
+    D = 8
+    q = rnd((1, 2, 6, D), 40)
+    # Skv = 1: O = v0, LSE = scale q.k0
+    k1, v1 = rnd((1, 2, 1, D), 41), rnd((1, 2, 1, D), 42)
+    O, L = attn(q, k1, v1, 0.5)
+    np.testing.assert_allclose(O, np.broadcast_to(v1, O.shape), rtol=0, atol=TOL)
+    np.testing.assert_allclose(L, 0.5 * np.einsum("bhid,bhd->bhi", q, k1[:, :, 0]), rtol=0, atol=TOL)
+    # all keys identical: uniform P, O = mean of V, LSE = scale q.k + ln Skv
+    Skv = 13
+    kk = np.repeat(rnd((1, 2, 1, D), 43), Skv, axis=2)
+    vv = rnd((1, 2, Skv, D), 44)
+    O, L = attn(q, kk, vv, 0.9)
+    np.testing.assert_allclose(O, np.broadcast_to(vv.mean(axis=2, keepdims=True), O.shape), rtol=0, atol=TOL)
+    np.testing.assert_allclose(L, 0.9 * np.einsum("bhid,bhd->bhi", q, kk[:, :, 0]) + math.log(Skv),
+                               rtol=0, atol=TOL)
+    # V = 1: every output is 1 (rows of P sum to one)
+    O, _ = attn(q, rnd((1, 2, Skv, D), 45), np.ones((1, 2, Skv, D)), 0.3)
+    np.testing.assert_allclose(O, 1.0, rtol=0, atol=TOL)
+    # K = 0: LSE = ln Skv
+    _, L = attn(q, np.zeros((1, 2, Skv, D)), vv, 0.3)
+    np.testing.assert_allclose(L, math.log(Skv), rtol=0, atol=TOL)
+    # two keys, hand-derived: z = (1, 0) -> P = (e, 1)/(e + 1)
+    qh = np.array([1.0, 0.0]).reshape(1, 1, 1, 2)
+    kh = np.array([[1.0, 0.0], [0.0, 1.0]]).reshape(1, 1, 2, 2)
+    vh = np.array([[2.0, -1.0], [4.0, 3.0]]).reshape(1, 1, 2, 2)
+    O, L = attn(qh, kh, vh, 1.0)
+    e = math.e
+    np.testing.assert_allclose(O[0, 0, 0], [(2 * e + 4) / (e + 1), (-e + 3) / (e + 1)], rtol=0, atol=TOL)
+    np.testing.assert_allclose(L[0, 0, 0], math.log(e + 1), rtol=0, atol=TOL)
+
+
+def pin_invariants(attn):
+    B, H, Sq, Skv, D = 1, 2, 10, 17, 8
+    q, k, v = rnd((B, H, Sq, D), 50), rnd((B, H, Skv, D), 51), rnd((B, H, Skv, D), 52)
+    s = 0.41
+    O, L = attn(q, k, v, s)
+    perm = np.random.Generator(np.random.PCG64(53)).permutation(Skv)
+    O2, L2 = attn(q, k[:, :, perm], v[:, :, perm], s)
+    np.testing.assert_allclose(O2, O, rtol=0, atol=TOL)
+    np.testing.assert_allclose(L2, L, rtol=0, atol=TOL)
+    qp = np.random.Generator(np.random.PCG64(54)).permutation(Sq)
+    O3, L3 = attn(q[:, :, qp], k, v, s)
+    np.testing.assert_allclose(O3, O[:, :, qp], rtol=0, atol=TOL)
+    np.testing.assert_allclose(L3, L[:, :, qp], rtol=0, atol=TOL)
+    u = rnd((B, H, 1, D), 55)
+    O4, L4 = attn(q, k + u, v, s)
+    np.testing.assert_allclose(O4, O, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(L4, L + s * np.einsum("bhid,bhd->bhi", q, u[:, :, 0]), rtol=0, atol=1e-11)
+    # large scores (|z| ~ 1e3) stay finite and match the shifted small-score case
+    O5, L5 = attn(q * 300.0, k, v, s)
+    assert np.all(np.isfinite(O5)) and np.all(np.isfinite(L5))
+
+
+ALL_PINS = [pin_brute_force, pin_library_sdpa, pin_closed_forms, pin_invariants]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_attention_pins(pin):
+    pin(oracle.attention)
+
+
+def test_attention_rows_matches_full():
+    q, k, v = rnd((1, 2, 40, 8), 60), rnd((1, 2, 33, 8), 61), rnd((1, 2, 33, 8), 62)
+    O, L = oracle.attention(q, k, v, 0.3)
+    rows = [0, 5, 39, 17]
+    Or, Lr = oracle.attention_rows(q, k, v, 0.3, rows)
+    np.testing.assert_array_equal(Or, O[:, :, rows])
+    np.testing.assert_array_equal(Lr, L[:, :, rows])
+
+
+def test_empty_keys():
+    q = rnd((1, 1, 3, 4), 63)
+    O, L = oracle.attention(q, np.zeros((1, 1, 0, 4)), np.zeros((1, 1, 0, 4)), 0.5)
+    assert np.all(O == 0) and np.all(np.isneginf(L))
+
+
+def test_statistical_sanity():
+    # N(0,1) inputs with scale 1/sqrt(D): scores ~ N(0,1), so E[LSE] ~ ln Skv + 1/2.
+    D, Skv = 64, 4096
+    q, k, v = rnd((1, 1, 64, D), 64), rnd((1, 1, Skv, D), 65), rnd((1, 1, Skv, D), 66)
+    O, L = oracle.attention(q, k, v, 1 / math.sqrt(D))
+    assert abs(L.mean() - (math.log(Skv) + 0.5)) < 0.1
+    assert 0.5 * math.sqrt(math.e / Skv) < O.std() < 1.5 * math.sqrt(math.e / Skv)
+
+
+# --------------------------------------------------------------- planted mistakes
+def _mutant(kind):
+    def attn(q, k, v, scale):
+        q = np.asarray(q, float)
+        k = np.asarray(k, float)
+        v = np.asarray(v, float)
+        B, H, Sq, D = q.shape
+        O = np.zeros((B, H, Sq, v.shape[3]))
+        L = np.zeros((B, H, Sq))
+        for b in range(B):
+            for h in range(H):
+                sc = 1.0 if kind == "drop_scale" else scale
+                z = sc * (q[b, h] @ k[b, h].T)
+                m = z.max(axis=1)
+                if kind == "lse_sign":
+                    lse = m - np.log(np.exp(z - m[:, None]).sum(axis=1))
+                elif kind == "lse_no_max":
+                    lse = np.log(np.exp(z - m[:, None]).sum(axis=1))
+                else:
+                    lse = m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+                p = np.exp(z - (m[:, None] if kind == "no_normalise" else lse[:, None]))
+                vv = v[b, h]
+                if kind == "v_off_by_one":
+                    vv = np.roll(vv, 1, axis=0)
+                if kind == "drop_last_key":
+                    p[:, -1] = 0.0
+                O[b, h] = p @ vv
+                L[b, h] = lse
+        return O, L
+    return attn
+
+
+@pytest.mark.parametrize("kind", ["drop_scale", "lse_sign", "lse_no_max", "no_normalise",
+                                  "v_off_by_one", "drop_last_key"])
+def test_pins_catch_planted_mistakes(kind):
+    mutant = _mutant(kind)
+    failures = 0
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"no pin caught the planted mistake {kind!r}"
+
+
+def test_unmutated_copy_passes_pins():
+    # the mutation harness itself is faithful when no mistake is planted
+    good = _mutant("none")
+    for pin in ALL_PINS:
+        pin(good)
+
+
+# ----------------------------------------------------------------------- merge
+def test_merge_equals_unchunked():
+    B, H, Sq, D = 1, 2, 20, 8
+    q = rnd((B, H, Sq, D), 70)
+    k, v = rnd((B, H, 57, D), 71), rnd((B, H, 57, D), 72)
+    s = 0.35
+    O, L = oracle.attention(q, k, v, s)
+    # two chunks, then eight uneven chunks folded left to right
+    Oa, La = oracle.attention(q, k[:, :, :20], v[:, :, :20], s)
+    Ob, Lb = oracle.attention(q, k[:, :, 20:], v[:, :, 20:], s)
+    Om, Lm = oracle.merge(Oa, La, Ob, Lb)
+    np.testing.assert_allclose(Om, O, rtol=0, atol=TOL)
+    np.testing.assert_allclose(Lm, L, rtol=0, atol=TOL)
+    edges = [0, 3, 10, 11, 30, 31, 44, 50, 57]
+    acc = (np.zeros_like(O), np.full(L.shape, -np.inf))
+    for a, b in zip(edges[:-1], edges[1:]):
+        Oc, Lc = oracle.attention(q, k[:, :, a:b], v[:, :, a:b], s)
+        acc = oracle.merge(acc[0], acc[1], Oc, Lc)
+    np.testing.assert_allclose(acc[0], O, rtol=0, atol=TOL)
+    np.testing.assert_allclose(acc[1], L, rtol=0, atol=TOL)
+
+
+def test_merge_algebra():
+    o1, l1 = rnd((2, 5, 4), 80), rnd((2, 5), 81) * 3
+    o2, l2 = rnd((2, 5, 4), 82), rnd((2, 5), 83) * 3
+    o3, l3 = rnd((2, 5, 4), 84), rnd((2, 5), 85) * 3
+    zero, ninf = np.zeros_like(o1), np.full(l1.shape, -np.inf)
+    oi, li = oracle.merge(o1, l1, zero, ninf)                 # identity
+    np.testing.assert_array_equal(oi, o1)
+    np.testing.assert_array_equal(li, l1)
+    oa, la = oracle.merge(o1, l1, o2, l2)                     # commutativity
+    ob, lb = oracle.merge(o2, l2, o1, l1)
+    np.testing.assert_allclose(oa, ob, rtol=0, atol=TOL)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=TOL)
+    x = oracle.merge(*oracle.merge(o1, l1, o2, l2), o3, l3)   # associativity
+    y = oracle.merge(o1, l1, *oracle.merge(o2, l2, o3, l3))
+    np.testing.assert_allclose(x[0], y[0], rtol=0, atol=TOL)
+    np.testing.assert_allclose(x[1], y[1], rtol=0, atol=TOL)
+    oe, le = oracle.merge(zero, ninf, zero, ninf)             # both empty
+    assert np.all(oe == 0) and np.all(np.isneginf(le))
+    # equal LSE: weights one half each, LSE + ln 2
+    om, lm = oracle.merge(o1, l1, o2, l1)
+    np.testing.assert_allclose(om, 0.5 * (o1 + o2), rtol=0, atol=TOL)
+    np.testing.assert_allclose(lm, l1 + math.log(2), rtol=0, atol=TOL)
+
+
+# -------------------------------------------------------------------- relayout
+def loop_pack_s2h(src, P):
+    B, S_l, H, D = src.shape
+    Hp = H // P
+    dst = np.zeros((B, P, S_l, Hp, D), src.dtype)
+    for b in range(B):
+        for p in range(P):
+            for s in range(S_l):
+                for h in range(Hp):
+                    dst[b, p, s, h, :] = src[b, s, p * Hp + h, :]
+    return dst
+
+
+def loop_unpack_s2h(src, P):
+    B, _, S_l, Hp, D = src.shape
+    dst = np.zeros((B, Hp, P * S_l, D), src.dtype)
+    for b in range(B):
+        for p in range(P):
+            for s in range(S_l):
+                for h in range(Hp):
+                    dst[b, h, p * S_l + s, :] = src[b, p, s, h, :]
+    return dst
+
+
+def loop_pack_h2s(src, P):
+    B, Hp, S, D = src.shape
+    S_l = S // P
+    dst = np.zeros((B, P, S_l, Hp, D), src.dtype)
+    for b in range(B):
+        for p in range(P):
+            for s in range(S_l):
+                for h in range(Hp):
+                    dst[b, p, s, h, :] = src[b, h, p * S_l + s, :]
+    return dst
+
+
+def loop_unpack_h2s(src, P):
+    B, _, S_l, Hp, D = src.shape
+    dst = np.zeros((B, S_l, P * Hp, D), src.dtype)
+    for b in range(B):
+        for g in range(P):
+            for s in range(S_l):
+                for h in range(Hp):
+                    dst[b, s, g * Hp + h, :] = src[b, g, s, h, :]
+    return dst
+
+
+@pytest.mark.parametrize("B,S_l,H,D,P", [(1, 5, 6, 4, 3), (2, 7, 8, 2, 4), (1, 3, 24, 8, 8)])
+def test_relayout_index_maps(B, S_l, H, D, P):
+    src = np.arange(B * S_l * H * D, dtype=np.int64).reshape(B, S_l, H, D)
+    s2h = oracle.ulysses_pack(src, P, oracle.SEQ_TO_HEAD)
+    np.testing.assert_array_equal(s2h, loop_pack_s2h(src, P))
+    u = oracle.ulysses_unpack(s2h, P, oracle.SEQ_TO_HEAD)
+    np.testing.assert_array_equal(u, loop_unpack_s2h(s2h, P))
+    hs = np.arange(B * (H // P) * P * S_l * D, dtype=np.int64).reshape(B, H // P, P * S_l, D)
+    h2s = oracle.ulysses_pack(hs, P, oracle.HEAD_TO_SEQ)
+    np.testing.assert_array_equal(h2s, loop_pack_h2s(hs, P))
+    np.testing.assert_array_equal(oracle.ulysses_unpack(h2s, P, oracle.HEAD_TO_SEQ), loop_unpack_h2s(h2s, P))
+    # bijections: every source element appears exactly once
+    assert np.array_equal(np.sort(s2h.ravel()), np.arange(src.size))
+    assert np.array_equal(np.sort(h2s.ravel()), np.arange(hs.size))
+    # head->seq pack inverts seq->head unpack, head->seq unpack inverts seq->head pack
+    np.testing.assert_array_equal(oracle.ulysses_pack(u, P, oracle.HEAD_TO_SEQ), s2h)
+    np.testing.assert_array_equal(oracle.ulysses_unpack(s2h, P, oracle.HEAD_TO_SEQ), src)
+
+
+def test_alltoall_is_chunk_transpose():
+    P = 4
+    send = [np.arange(P * 3).reshape(1, P, 3) + 100 * p for p in range(P)]
+    recv = oracle.alltoall(send)
+    for r in range(P):
+        for p in range(P):
+            np.testing.assert_array_equal(recv[r][:, p], send[p][:, r])
+    back = oracle.alltoall(recv)
+    for p in range(P):
+        np.testing.assert_array_equal(back[p], send[p])
+
+
+def test_simulated_ulysses_pipeline_equals_direct_attention():
+    """pack -> a2a -> unpack -> attention per head subset -> pack -> a2a -> unpack
+    equals attention over all heads for every rank's tokens."""
+    P, S_l, H, D = 4, 6, 8, 8
+    S = P * S_l
+    q, k, v = (rnd((1, S, H, D), s) for s in (90, 91, 92))   # token-major global tensors
+    scale = 1 / math.sqrt(D)
+    shards = [(q[:, r * S_l:(r + 1) * S_l], k[:, r * S_l:(r + 1) * S_l], v[:, r * S_l:(r + 1) * S_l])
+              for r in range(P)]
+    recv = []
+    for t in range(3):
+        send = [oracle.ulysses_pack(shards[r][t], P, oracle.SEQ_TO_HEAD) for r in range(P)]
+        recv.append([oracle.ulysses_unpack(x, P, oracle.SEQ_TO_HEAD) for x in oracle.alltoall(send)])
+    outs = []
+    for r in range(P):
+        qh, kh, vh = recv[0][r], recv[1][r], recv[2][r]        # [1, Hp, S, D]
+        O, _ = oracle.attention(qh, kh, vh, scale)
+        outs.append(oracle.ulysses_pack(O, P, oracle.HEAD_TO_SEQ))
+    back = [oracle.ulysses_unpack(x, P, oracle.HEAD_TO_SEQ) for x in oracle.alltoall(outs)]
+    O_direct, _ = oracle.attention(q.transpose(0, 2, 1, 3), k.transpose(0, 2, 1, 3),
+                                   v.transpose(0, 2, 1, 3), scale)      # [1, H, S, D]
+    for r in range(P):
+        np.testing.assert_allclose(back[r], O_direct.transpose(0, 2, 1, 3)[:, r * S_l:(r + 1) * S_l],
+                                   rtol=0, atol=TOL)
+
+
+# ------------------------------------------------------------------ input recipe
+def test_bf16_rounding_rne():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 2 ** -7 + 2 ** -8, -3.140625, 1.0 + 3 * 2 ** -9], np.float32)
+    b = inputs.f32_to_bf16_bits(x)
+    back = inputs.bf16_bits_to_f32(b)
+    # 1 + 2^-8 is a tie -> even (1.0); 1 + 2^-7 + 2^-8 is a tie -> even (1 + 2^-6)
+    np.testing.assert_array_equal(back, np.array([1.0, 1.0, 1.0 + 2 ** -6, -3.140625, 1.0 + 2 ** -7], np.float32))
+    # matches torch's own float32 -> bfloat16 conversion (round to nearest even)
+    y = inputs.normal_f32((4096,), np.random.Generator(np.random.PCG64(3)))
+    tb = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(inputs.f32_to_bf16_bits(y), tb)
+
+
+def test_inputs_are_seeded():
+    a = inputs.small_f32_set()
+    b = inputs.small_f32_set()
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    assert a[0].shape == (1, 2, 256, 64) and a[0].dtype == np.float32
+    assert abs(float(a[0].std()) - 1.0) < 0.05
