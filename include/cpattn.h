@@ -1,0 +1,193 @@
+/*
+ * cpattn -- per-rank attention for context-parallel diffusion transformers
+ * on AMD Instinct MI355X (gfx950).  C ABI, version 1.
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *
+ *  - attn_fwd: non-causal multi-head scaled dot-product attention returning
+ *    O and the per-row natural log-sum-exp of the scaled scores.  Diffusion
+ *    transformers attend bidirectionally, with no causal mask ("Scaling AI
+ *    inference across multiple GPUs using NVIDIA TensorRT with multi-device
+ *    inference support", section "Context parallelism"); the score chain is
+ *    scaled QK^T -> softmax -> times V with a total scale of 1/sqrt(head_dim)
+ *    ("TensorRT multi-device attention inference in practice", step 1).
+ *    Context parallelism divides this work per rank: AllGather-KV gives a
+ *    rank its query rows against all keys, Ulysses gives it all rows of a
+ *    head subset, and Ring Attention gives it one K/V chunk at a time (first
+ *    page, sections "AllGather KV", "Ring Attention", "DeepSpeed Ulysses").
+ *
+ *  - attn_merge: combines two partial results (O, LSE) over disjoint key
+ *    sets into the result over their union -- the online-softmax step that
+ *    lets Ring Attention stream K/V chunks (first page, "Ring Attention").
+ *
+ *  - ring_attn_fwd: the per-rank ring loop on one device: attention of the
+ *    local queries against each of n K/V chunks in turn, folded with
+ *    attn_merge (first page, "Ring Attention").
+ *
+ *  - ulysses_pack / ulysses_unpack: the sequence<->head relayout on either
+ *    side of DeepSpeed Ulysses' two all-to-alls (first page, "DeepSpeed
+ *    Ulysses"; 5520 tokens per rank at degree 8 in "Simplifying model
+ *    serving across multiple GPUs with NVIDIA TensorRT multi-device
+ *    integration in NVIDIA Dynamo-Triton", section on distributing Cosmos 3
+ *    with Ulysses context parallelism).
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous
+ *    (row-major, last dimension fastest) and 16-byte aligned.  The library
+ *    never allocates, frees or retains memory, keeps no state between calls
+ *    and has no handles.
+ *  - Work is enqueued on the caller's HIP stream (0 = the null stream) and
+ *    runs asynchronously; the call returns once the launches are enqueued.
+ *  - Argument checks run synchronously, on the host, before any HIP call.
+ *    A failed check returns its status and enqueues nothing.  A launch
+ *    failure returns CPATTN_E_HIP.  Faults inside a kernel surface at the
+ *    caller's next synchronisation on the stream.
+ *  - Sizes are int64_t; every element count must stay below 2^62 and every
+ *    per-dimension size below 2^31.
+ *  - Functions are reentrant and thread-safe.  Calls on different streams
+ *    may run concurrently as long as their buffers do not overlap.
+ *
+ * bf16 is the 16-bit brain-float format stored as raw 16-bit words; f32 is
+ * IEEE binary32.
+ */
+#ifndef CPATTN_H_
+#define CPATTN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPATTN_ABI_VERSION 1
+
+typedef enum {
+    CPATTN_OK = 0,
+    CPATTN_E_NULL = 1,     /* a required pointer is NULL                          */
+    CPATTN_E_SHAPE = 2,    /* a size is out of range, inconsistent or overflows   */
+    CPATTN_E_DTYPE = 3,    /* unsupported dtype or dtype combination              */
+    CPATTN_E_HEADDIM = 4,  /* head dimension D not supported by the kernel        */
+    CPATTN_E_ALIGN = 5,    /* a pointer is not 16-byte aligned                    */
+    CPATTN_E_ALIAS = 6,    /* buffers overlap where overlap is not allowed        */
+    CPATTN_E_HIP = 7,      /* the HIP runtime rejected a launch                   */
+    CPATTN_E_SCALE = 8     /* the score scale is not a finite positive number     */
+} cpattn_status;
+
+typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
+
+typedef enum { CPATTN_SEQ_TO_HEAD = 0, CPATTN_HEAD_TO_SEQ = 1 } cpattn_dir;
+
+/*
+ * Non-causal attention forward with per-row LSE.
+ *
+ *   q   [B, H, Sq,  D]  in_dtype         k, v [B, H, Skv, D]  in_dtype
+ *   o   [B, H, Sq,  D]  o_dtype (output)  lse  [B, H, Sq]      f32 (output)
+ *
+ *   z_ij   = scale * sum_d q_id k_jd
+ *   LSE_i  = ln sum_j exp(z_ij)                 (computed max-shifted)
+ *   O_id   = sum_j exp(z_ij - LSE_i) v_jd
+ *
+ * No mask of any kind.  Skv = 0 is allowed and yields O = 0, LSE = -inf
+ * (the identity of attn_merge).  B, H, Sq >= 1; Skv >= 0; D in {64, 128};
+ * scale finite and > 0 (1/sqrt(D) is the usual choice).
+ *
+ * dtypes: in_dtype = BF16 with o_dtype = BF16 (bf16 matrix cores, fp32
+ * accumulation and softmax state, softmax weights rounded to bf16 for the PV
+ * product, O rounded to nearest even) or o_dtype = F32 (the same computation
+ * with O kept in f32, e.g. for ring partials); in_dtype = F32 requires
+ * o_dtype = F32 (all arithmetic in f32).  Any other pair -> CPATTN_E_DTYPE.
+ *
+ * o and lse must not overlap each other or q, k, v (CPATTN_E_ALIAS).
+ */
+cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                              float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
+                              hipStream_t stream);
+
+/*
+ * Merge two partial attention results over disjoint key sets a and b.
+ *
+ *   o_a, o_b, o_out  [B, H, S, D]  o_dtype      lse_a, lse_b, lse_out  [B, H, S]  f32
+ *
+ *   M   = max(La, Lb)
+ *   L   = M + ln(exp(La - M) + exp(Lb - M))
+ *   O   = exp(La - L) * Oa + exp(Lb - L) * Ob
+ *
+ * computed in f32 and stored in o_dtype (bf16 rounded to nearest even).
+ * An empty side (LSE = -inf, O = 0) is the identity; two empty sides give
+ * O = 0, LSE = -inf.  o_out may be exactly o_a or exactly o_b, and lse_out
+ * exactly lse_a or lse_b (in-place accumulation); any other overlap is
+ * CPATTN_E_ALIAS.  B, H, S >= 1; D >= 8 with D*sizeof(o_dtype) a multiple of
+ * 16 bytes and D <= 1024.
+ */
+cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                                void* o_out, float* lse_out, int64_t B, int64_t H, int64_t S, int64_t D,
+                                cpattn_dtype o_dtype, hipStream_t stream);
+
+/*
+ * Ring Attention on one rank, stream-ordered on one device.
+ *
+ *   q         [B, H, Sq, D]                      bf16
+ *   k_chunks  [n_chunks, B, H, Skv_chunk, D]     bf16  (chunk c = the c-th block of keys
+ *   v_chunks  [n_chunks, B, H, Skv_chunk, D]     bf16   a ring would deliver)
+ *   o         [B, H, Sq, D]  f32 (output)          lse  [B, H, Sq] f32 (output)
+ *   o_work    [B, H, Sq, D]  f32 (caller-owned scratch)
+ *   lse_work  [B, H, Sq]     f32 (caller-owned scratch)
+ *
+ * Chunk 0's attention is written to (o, lse); every later chunk's attention
+ * goes to (o_work, lse_work) and is merged into (o, lse) in place.  The
+ * result equals attention over the concatenation of all chunks.  n_chunks
+ * >= 1, Skv_chunk >= 0, D in {64, 128}, scale as for attn_fwd.  o, lse,
+ * o_work and lse_work must not overlap each other or the inputs.
+ */
+cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_chunks, const void* v_chunks,
+                                   float* o, float* lse, float* o_work, float* lse_work,
+                                   int64_t B, int64_t H, int64_t Sq, int64_t Skv_chunk, int64_t n_chunks,
+                                   int64_t D, float scale, hipStream_t stream);
+
+/*
+ * Ulysses relayout, packing side (builds the all-to-all send buffer).
+ * Hp = H / P, S = P * S_local.
+ *
+ *   SEQ_TO_HEAD: src [B, S_local, H, D]  ->  dst [B, P, S_local, Hp, D]
+ *                dst[b,p,s,h,:] = src[b,s,p*Hp+h,:]
+ *   HEAD_TO_SEQ: src [B, Hp, S, D]       ->  dst [B, P, S_local, Hp, D]
+ *                dst[b,p,s,h,:] = src[b,h,p*S_local+s,:]
+ *
+ * Chunk p of dst is destined for rank p.  A bit-exact copy of elements of
+ * type dt.  H % P == 0 (else CPATTN_E_SHAPE); D*sizeof(dt) a multiple of 16
+ * bytes; src and dst must not overlap.  Rank r is taken to own tokens
+ * [r*S_local, (r+1)*S_local) and heads [r*Hp, (r+1)*Hp).
+ */
+cpattn_status cpattn_ulysses_pack(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H,
+                                  int64_t D, int64_t P, cpattn_dtype dt, cpattn_dir dir,
+                                  hipStream_t stream);
+
+/*
+ * Ulysses relayout, unpacking side (reads the all-to-all receive buffer,
+ * whose chunk p came from rank p).
+ *
+ *   SEQ_TO_HEAD: src [B, P, S_local, Hp, D]  ->  dst [B, Hp, S, D]
+ *                dst[b,h,p*S_local+s,:] = src[b,p,s,h,:]
+ *   HEAD_TO_SEQ: src [B, P, S_local, Hp, D]  ->  dst [B, S_local, H, D]
+ *                dst[b,s,g*Hp+h,:] = src[b,g,s,h,:]
+ *
+ * Same requirements as cpattn_ulysses_pack.
+ */
+cpattn_status cpattn_ulysses_unpack(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H,
+                                    int64_t D, int64_t P, cpattn_dtype dt, cpattn_dir dir,
+                                    hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* cpattn_status_string(cpattn_status s);
+
+/* Returns CPATTN_ABI_VERSION of the built library. */
+int cpattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H_ */

@@ -1,1 +1,162 @@
-"""MI355X-native per-rank attention for context-parallel diffusion transformers."""
+"""MI355X-native per-rank attention for context-parallel diffusion transformers.
+
+Python binding of libcpattn (include/cpattn.h).  Every function only checks
+and marshals torch tensors (device pointers, sizes, the current HIP stream)
+and calls the C ABI; all computation runs in the library's HIP kernels.
+torch provides device memory and streams.
+
+  attn_fwd(q, k, v, o=None, lse=None, scale=None)        -> (o, lse)
+  attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None) -> (o_out, lse_out)
+  ring_attn_fwd(q, k_chunks, v_chunks, ...)               -> (o, lse)
+  ulysses_pack(src, P, direction, dst=None)               -> dst
+  ulysses_unpack(src, P, direction, dst=None)             -> dst
+"""
+from __future__ import annotations
+
+import math
+
+from ._lib import (BF16, F32, HEAD_TO_SEQ, SEQ_TO_HEAD, CpattnError, check, lib)
+
+__all__ = ["attn_fwd", "attn_merge", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
+           "SEQ_TO_HEAD", "HEAD_TO_SEQ", "CpattnError", "lib"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def attn_fwd(q, k, v, o=None, lse=None, scale=None, out_dtype=None, stream=None):
+    """Non-causal attention with per-row LSE.  q [B,H,Sq,D], k/v [B,H,Skv,D]."""
+    torch = _torch()
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if k.shape != (B, H, Skv, D) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o is None:
+        o = torch.empty((B, H, Sq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if o.shape != q.shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
+        raise ValueError("o must be [B,H,Sq,D] and lse float32 [B,H,Sq]")
+    st = lib().cpattn_attn_fwd(_dev(q, "q"), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
+                               _dev(o, "o"), _dev(lse, "lse"), B, H, Sq, Skv, D, float(scale),
+                               _dtype_code(q), _dtype_code(o), _stream(stream))
+    check("cpattn_attn_fwd", st)
+    return o, lse
+
+
+def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
+    """Merge two partial results over disjoint key sets; o_out may be o_a (in place)."""
+    torch = _torch()
+    B, H, S, D = o_a.shape
+    if o_b.shape != o_a.shape or lse_a.shape != (B, H, S) or lse_b.shape != (B, H, S):
+        raise ValueError("merge operands must share shapes")
+    if o_b.dtype != o_a.dtype:
+        raise TypeError("o_a and o_b must share a dtype")
+    if o_out is None:
+        o_out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    if o_out.dtype != o_a.dtype or o_out.shape != o_a.shape or lse_out.shape != lse_a.shape:
+        raise ValueError("outputs must match the operands")
+    for t in (lse_a, lse_b, lse_out):
+        if t.dtype != torch.float32:
+            raise TypeError("lse tensors must be float32")
+    st = lib().cpattn_attn_merge(_dev(o_a, "o_a"), _dev(lse_a, "lse_a"), _dev(o_b, "o_b"), _dev(lse_b, "lse_b"),
+                                 _dev(o_out, "o_out"), _dev(lse_out, "lse_out"), B, H, S, D,
+                                 _dtype_code(o_a), _stream(stream))
+    check("cpattn_attn_merge", st)
+    return o_out, lse_out
+
+
+def ring_attn_fwd(q, k_chunks, v_chunks, o=None, lse=None, o_work=None, lse_work=None, scale=None,
+                  stream=None):
+    """Ring attention over K/V chunks [n, B, H, Skv_chunk, D] (bf16); f32 O and LSE out."""
+    torch = _torch()
+    B, H, Sq, D = q.shape
+    n, B2, H2, Skv_c, D2 = k_chunks.shape
+    if (B2, H2, D2) != (B, H, D) or v_chunks.shape != k_chunks.shape:
+        raise ValueError("chunk shapes must be [n, B, H, Skv_chunk, D]")
+    if q.dtype != torch.bfloat16 or k_chunks.dtype != torch.bfloat16 or v_chunks.dtype != torch.bfloat16:
+        raise TypeError("ring_attn_fwd takes bfloat16 q and chunks")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    o = o if o is not None else torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
+    lse = lse if lse is not None else torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    if n > 1:
+        o_work = o_work if o_work is not None else torch.empty_like(o)
+        lse_work = lse_work if lse_work is not None else torch.empty_like(lse)
+    st = lib().cpattn_ring_attn_fwd(_dev(q, "q"), k_chunks.data_ptr() if Skv_c else None,
+                                    v_chunks.data_ptr() if Skv_c else None, _dev(o, "o"), _dev(lse, "lse"),
+                                    _dev(o_work, "o_work") if n > 1 else None,
+                                    _dev(lse_work, "lse_work") if n > 1 else None,
+                                    B, H, Sq, Skv_c, n, D, float(scale), _stream(stream))
+    check("cpattn_ring_attn_fwd", st)
+    return o, lse
+
+
+def _relayout_shapes(src, P, direction, pack):
+    if pack and direction == SEQ_TO_HEAD:
+        B, S_l, H, D = src.shape
+        return (B, S_l, H, D), (B, P, S_l, H // P, D)
+    if pack and direction == HEAD_TO_SEQ:
+        B, Hp, S, D = src.shape
+        return (B, S // P, Hp * P, D), (B, P, S // P, Hp, D)
+    B, P2, S_l, Hp, D = src.shape
+    if P2 != P:
+        raise ValueError("src chunk dim must equal P")
+    if direction == SEQ_TO_HEAD:
+        return (B, S_l, Hp * P, D), (B, Hp, P * S_l, D)
+    return (B, S_l, Hp * P, D), (B, S_l, Hp * P, D)
+
+
+def _relayout(fn, src, P, direction, dst, pack, stream):
+    torch = _torch()
+    (B, S_l, H, D), out_shape = _relayout_shapes(src, P, direction, pack)
+    if dst is None:
+        dst = torch.empty(out_shape, dtype=src.dtype, device=src.device)
+    if tuple(dst.shape) != tuple(out_shape) or dst.dtype != src.dtype:
+        raise ValueError(f"dst must be {out_shape} of {src.dtype}")
+    st = getattr(lib(), fn)(_dev(src, "src"), _dev(dst, "dst"), B, S_l, H, D, P, _dtype_code(src), direction,
+                            _stream(stream))
+    check(fn, st)
+    return dst
+
+
+def ulysses_pack(src, P, direction, dst=None, stream=None):
+    """seq->head: [B,S_l,H,D] -> [B,P,S_l,H/P,D]; head->seq: [B,Hp,S,D] -> [B,P,S/P,Hp,D]."""
+    return _relayout("cpattn_ulysses_pack", src, P, direction, dst, True, stream)
+
+
+def ulysses_unpack(src, P, direction, dst=None, stream=None):
+    """seq->head: [B,P,S_l,Hp,D] -> [B,Hp,P*S_l,D]; head->seq: [B,P,S_l,Hp,D] -> [B,S_l,P*Hp,D]."""
+    return _relayout("cpattn_ulysses_unpack", src, P, direction, dst, False, stream)

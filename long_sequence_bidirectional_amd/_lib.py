@@ -1,0 +1,65 @@
+"""ctypes loader for libcpattn.so (the C ABI declared in include/cpattn.h).
+
+Loading fails loudly if the library has not been built: there is no
+fallback implementation of any entry point.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libcpattn.so")
+
+# enum values of include/cpattn.h
+OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_ALIGN, E_ALIAS, E_HIP, E_SCALE = range(9)
+BF16, F32 = 0, 1
+SEQ_TO_HEAD, HEAD_TO_SEQ = 0, 1
+ABI_VERSION = 1
+
+STATUS_NAMES = {OK: "OK", E_NULL: "E_NULL", E_SHAPE: "E_SHAPE", E_DTYPE: "E_DTYPE", E_HEADDIM: "E_HEADDIM",
+                E_ALIGN: "E_ALIGN", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP", E_SCALE: "E_SCALE"}
+
+# (name, restype, argtypes) of every exported function
+_P, _I64, _F, _E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+SIGNATURES = [
+    ("cpattn_attn_fwd", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _P]),
+    ("cpattn_attn_merge", _E, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _E, _P]),
+    ("cpattn_ring_attn_fwd", _E, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P]),
+    ("cpattn_ulysses_pack", _E, [_P, _P, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),
+    ("cpattn_ulysses_unpack", _E, [_P, _P, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),
+    ("cpattn_status_string", ctypes.c_char_p, [_E]),
+    ("cpattn_abi_version", ctypes.c_int, []),
+]
+
+_lib = None
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} ({message})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument types set (loaded once per process)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m long_sequence_bidirectional_amd.build` "
+                "(there is no fallback implementation)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            f = getattr(handle, name)
+            f.restype = res
+            f.argtypes = args
+        if handle.cpattn_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH}: ABI version {handle.cpattn_abi_version()} != {ABI_VERSION}")
+        _lib = handle
+    return _lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != OK:
+        raise CpattnError(fn, status, lib().cpattn_status_string(status).decode())

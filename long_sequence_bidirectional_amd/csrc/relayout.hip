@@ -1,0 +1,99 @@
+// Ulysses sequence<->head relayout (pack before / unpack after each all-to-all).
+//
+// DeepSpeed Ulysses swaps a sequence split for a head split with one
+// all-to-all before attention and swaps back with a second one after it
+// ("Scaling AI inference across multiple GPUs using NVIDIA TensorRT with
+// multi-device inference support", section "DeepSpeed Ulysses").  Around each
+// exchange a rank reorders whole D-vectors ("rows") between its token-major
+// shard, the [P, S_local, Hp] send/receive buffer and the head-major
+// full-sequence layout that attention reads.  The four maps (row indices,
+// Hp = H / P):
+//   mode 0  pack   seq->head  dst[b,p,s,h]        <- src[b,s,p*Hp+h]
+//   mode 1  unpack seq->head  dst[b,h,p*S_l+s]    <- src[b,p,s,h]
+//   mode 2  pack   head->seq  dst[b,p,s,h]        <- src[b,h,p*S_l+s]
+//   mode 3  unpack head->seq  dst[b,s,g*Hp+h]     <- src[b,g,s,h]
+//
+// A pure copy, so HBM-bound: every byte is read once and written once.  The
+// kernel walks dst in order; each row is a contiguous run of row_bytes (a
+// multiple of 16) in both buffers, moved with 16-byte loads and stores by
+// consecutive lanes.  The source row index is derived once per row.
+#include "common.h"
+#include "kernels.h"
+
+namespace cpattn {
+namespace {
+
+__device__ __forceinline__ uint32_t src_row_of(uint32_t r, int mode, uint32_t S_l, uint32_t H, uint32_t Hp,
+                                               uint32_t P) {
+    if (mode == 0 || mode == 2) {
+        const uint32_t h = r % Hp;
+        uint32_t t = r / Hp;
+        const uint32_t s = t % S_l;
+        t /= S_l;
+        const uint32_t p = t % P;
+        const uint32_t b = t / P;
+        return mode == 0 ? (b * S_l + s) * H + p * Hp + h : (b * Hp + h) * (P * S_l) + p * S_l + s;
+    }
+    if (mode == 1) {
+        const uint32_t S = P * S_l;
+        const uint32_t ts = r % S;
+        const uint32_t t = r / S;
+        const uint32_t h = t % Hp;
+        const uint32_t b = t / Hp;
+        const uint32_t p = ts / S_l;
+        const uint32_t s = ts - p * S_l;
+        return ((b * P + p) * S_l + s) * Hp + h;
+    }
+    const uint32_t hg = r % H;
+    const uint32_t t = r / H;
+    const uint32_t s = t % S_l;
+    const uint32_t b = t / S_l;
+    const uint32_t g = hg / Hp;
+    const uint32_t h = hg - g * Hp;
+    return ((b * P + g) * S_l + s) * Hp + h;
+}
+
+// One thread per 16-byte chunk; chunks_per_row consecutive lanes share a row.
+__global__ __launch_bounds__(256) void relayout_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                       uint32_t n_rows, uint32_t chunks_per_row, int mode,
+                                                       uint32_t S_l, uint32_t H, uint32_t Hp, uint32_t P) {
+    const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t total = (uint64_t)n_rows * chunks_per_row;
+    if (gid >= total) return;
+    const uint32_t r = (uint32_t)(gid / chunks_per_row);
+    const uint32_t c = (uint32_t)(gid - (uint64_t)r * chunks_per_row);
+    const uint32_t sr = src_row_of(r, mode, S_l, H, Hp, P);
+    dst[(uint64_t)r * chunks_per_row + c] = src[(uint64_t)sr * chunks_per_row + c];
+}
+
+__global__ __launch_bounds__(256) void fill_empty_kernel(u32x4* __restrict__ o, uint64_t o_chunks,
+                                                         float* __restrict__ lse, uint64_t n_rows) {
+    const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid < o_chunks) o[gid] = u32x4{0, 0, 0, 0};
+    if (gid < n_rows) lse[gid] = -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_relayout(const RelayoutArgs& a) {
+    const uint32_t Hp = (uint32_t)(a.H / a.P);
+    const uint32_t chunks = (uint32_t)(a.row_bytes / 16);
+    const uint32_t n_rows = (uint32_t)(a.B * a.S_local * a.H);
+    const uint64_t total = (uint64_t)n_rows * chunks;
+    const uint64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(relayout_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream,
+                       static_cast<const u32x4*>(a.src), static_cast<u32x4*>(a.dst), n_rows, chunks, a.mode,
+                       (uint32_t)a.S_local, (uint32_t)a.H, Hp, (uint32_t)a.P);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_empty(void* o, int64_t o_bytes, float* lse, int64_t n_rows, hipStream_t stream) {
+    const uint64_t chunks = (uint64_t)o_bytes / 16;
+    const uint64_t n = chunks > (uint64_t)n_rows ? chunks : (uint64_t)n_rows;
+    const uint64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_empty_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<u32x4*>(o),
+                       chunks, lse, (uint64_t)n_rows);
+    return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU.
+
+The library must load, export every function include/cpattn.h declares, and
+reject bad arguments with the documented status before any HIP call.  The
+pointers passed here are fake addresses that are never dereferenced: every
+call below fails validation, so nothing is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_sequence_bidirectional_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+A = 0x10000000      # fake, 16-byte aligned, far apart
+B_ = 0x20000000
+C = 0x30000000
+D_ = 0x40000000
+E = 0x50000000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libcpattn.so not built (run python -m long_sequence_bidirectional_amd.build)")
+    return _lib.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpattn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert header_functions() == sorted(["cpattn_abi_version", "cpattn_attn_fwd", "cpattn_attn_merge",
+                                         "cpattn_ring_attn_fwd", "cpattn_status_string",
+                                         "cpattn_ulysses_pack", "cpattn_ulysses_unpack"])
+
+
+def test_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (cpattn_\w+)", out))
+    assert set(header_functions()) <= exported
+    # nothing else leaks out of the C ABI
+    assert {s for s in exported if s.startswith("cpattn")} == set(header_functions())
+    assert {name for name, _, _ in _lib.SIGNATURES} == set(header_functions())
+
+
+def test_version_and_status_strings(L):
+    assert L.cpattn_abi_version() == _lib.ABI_VERSION == 1
+    seen = set()
+    for s in range(9):
+        msg = L.cpattn_status_string(s)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert L.cpattn_status_string(99) == b"unknown status"
+
+
+def fwd(L, q=A, k=B_, v=C, o=D_, lse=E, B=1, H=2, Sq=256, Skv=256, D=64, scale=0.125, i=0, od=0):
+    return L.cpattn_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, i, od, None)
+
+
+def test_attn_fwd_validation(L):
+    assert fwd(L, q=None) == _lib.E_NULL
+    assert fwd(L, o=None) == _lib.E_NULL
+    assert fwd(L, lse=None) == _lib.E_NULL
+    assert fwd(L, k=None) == _lib.E_NULL
+    assert fwd(L, i=2) == _lib.E_DTYPE
+    assert fwd(L, i=_lib.F32, od=_lib.BF16) == _lib.E_DTYPE
+    assert fwd(L, D=96) == _lib.E_HEADDIM
+    assert fwd(L, D=256) == _lib.E_HEADDIM
+    assert fwd(L, B=0) == _lib.E_SHAPE
+    assert fwd(L, Sq=0) == _lib.E_SHAPE
+    assert fwd(L, Skv=-1) == _lib.E_SHAPE
+    assert fwd(L, H=1 << 31) == _lib.E_SHAPE
+    assert fwd(L, B=1 << 30, H=1 << 30, Sq=1 << 30) == _lib.E_SHAPE   # element count overflow
+    assert fwd(L, scale=0.0) == _lib.E_SCALE
+    assert fwd(L, scale=-0.1) == _lib.E_SCALE
+    assert fwd(L, scale=float("inf")) == _lib.E_SCALE
+    assert fwd(L, scale=float("nan")) == _lib.E_SCALE
+    assert fwd(L, q=A + 8) == _lib.E_ALIGN
+    assert fwd(L, lse=E + 4) == _lib.E_ALIGN
+    # o overlapping q, lse overlapping o, lse overlapping v
+    assert fwd(L, o=A + 16) == _lib.E_ALIAS
+    assert fwd(L, lse=D_ + 64) == _lib.E_ALIAS
+    assert fwd(L, lse=C + 1024) == _lib.E_ALIAS
+
+
+def merge(L, oa=A, la=B_, ob=C, lb=D_, oo=E, lo=0x60000000, B=1, H=2, S=100, D=128, dt=0):
+    return L.cpattn_attn_merge(oa, la, ob, lb, oo, lo, B, H, S, D, dt, None)
+
+
+def test_attn_merge_validation(L):
+    assert merge(L, oa=None) == _lib.E_NULL
+    assert merge(L, lo=None) == _lib.E_NULL
+    assert merge(L, dt=5) == _lib.E_DTYPE
+    assert merge(L, S=0) == _lib.E_SHAPE
+    assert merge(L, D=4) == _lib.E_HEADDIM
+    assert merge(L, D=12) == _lib.E_HEADDIM            # 24 bytes per row: not a multiple of 16
+    assert merge(L, D=2048) == _lib.E_HEADDIM
+    assert merge(L, oo=E + 2) == _lib.E_ALIGN
+    assert merge(L, oo=A + 256) == _lib.E_ALIAS        # partial overlap with o_a
+    assert merge(L, lo=B_ + 16) == _lib.E_ALIAS        # partial overlap with lse_a
+    assert merge(L, oo=B_) == _lib.E_ALIAS             # o_out on top of lse_a
+
+
+def ring(L, q=A, k=B_, v=C, o=D_, lse=E, ow=0x60000000, lw=0x70000000, n=8, Skv=64, D=128, scale=0.1):
+    return L.cpattn_ring_attn_fwd(q, k, v, o, lse, ow, lw, 1, 2, 64, Skv, n, D, scale, None)
+
+
+def test_ring_validation(L):
+    assert ring(L, q=None) == _lib.E_NULL
+    assert ring(L, ow=None) == _lib.E_NULL
+    assert ring(L, n=0) == _lib.E_SHAPE
+    assert ring(L, D=80) == _lib.E_HEADDIM
+    assert ring(L, scale=0.0) == _lib.E_SCALE
+    assert ring(L, lw=E + 16) == _lib.E_ALIAS          # workspace LSE overlaps LSE
+    assert ring(L, ow=B_ + 4096) == _lib.E_ALIAS       # workspace O overlaps the K chunks
+
+
+def rl(L, fn, src=A, dst=B_, B=1, S_l=5520, H=24, D=128, P=8, dt=0, d=0):
+    return getattr(L, fn)(src, dst, B, S_l, H, D, P, dt, d, None)
+
+
+@pytest.mark.parametrize("fn", ["cpattn_ulysses_pack", "cpattn_ulysses_unpack"])
+def test_relayout_validation(L, fn):
+    assert rl(L, fn, src=None) == _lib.E_NULL
+    assert rl(L, fn, dt=3) == _lib.E_DTYPE
+    assert rl(L, fn, H=20) == _lib.E_SHAPE             # H % P != 0
+    assert rl(L, fn, P=0) == _lib.E_SHAPE
+    assert rl(L, fn, d=2) == _lib.E_SHAPE
+    assert rl(L, fn, D=4) == _lib.E_HEADDIM            # 8-byte rows
+    assert rl(L, fn, dst=B_ + 8) == _lib.E_ALIGN
+    assert rl(L, fn, dst=A + 1024) == _lib.E_ALIAS
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libcpattn.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

@@ -1,0 +1,147 @@
+"""GPU parity of attn_fwd against the fp64 oracle (called through the C ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import long_sequence_bidirectional_amd as cp
+from long_sequence_bidirectional_amd import inputs
+from helpers import (assert_bf16_parity, assert_f32_parity, dev_bf16, dev_f32, f64_of_bf16, host64, log,
+                     scale_of, BF16_MAX_ABS)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ f32 path
+def test_f32_tiny_workload():
+    """B=1 H=2 S=256 D=64 fp32 self-attention, scale 1/8, full comparison."""
+    q, k, v = inputs.small_f32_set()
+    log("case: f32 tiny [1,2,256,64]")
+    o, lse = cp.attn_fwd(dev_f32(q), dev_f32(k), dev_f32(v), scale=1 / 8)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), 1 / 8)
+    assert_f32_parity(host64(o), host64(lse), O, L, "f32 tiny")
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,D", [(1, 3, 77, 130, 128), (2, 1, 33, 1, 64), (1, 2, 100, 31, 64),
+                                          (1, 1, 1, 257, 128), (1, 1, 64, 64, 64)])
+def test_f32_ragged(B, H, Sq, Skv, D):
+    log(f"case: f32 ragged B{B} H{H} Sq{Sq} Skv{Skv} D{D}")
+    seed = 1000 + Sq + Skv
+    q = inputs.random_f32((B, H, Sq, D), seed)
+    k = inputs.random_f32((B, H, Skv, D), seed + 1)
+    v = inputs.random_f32((B, H, Skv, D), seed + 2)
+    o, lse = cp.attn_fwd(dev_f32(q), dev_f32(k), dev_f32(v))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), scale_of(D))
+    assert_f32_parity(host64(o), host64(lse), O, L, "f32 ragged")
+
+
+# ----------------------------------------------------------------- bf16 path
+SMALL_BF16 = [
+    (1, 2, 300, 333, 128),    # several 256-row tiles + ragged Q tail, several 64-key blocks + ragged KV tail
+    (1, 1, 513, 1000, 64),
+    (2, 3, 256, 64, 128),     # exactly one tile and one block
+    (1, 1, 17, 5, 128),       # Sq < one wave's rows, Skv < one block
+    (1, 2, 1, 1, 64),         # single row, single key
+    (1, 1, 600, 2992, 128),   # the text-token count (48-key tail)
+]
+
+
+@pytest.mark.parametrize("out_f32", [False, True], ids=["o_bf16", "o_f32"])
+@pytest.mark.parametrize("B,H,Sq,Skv,D", SMALL_BF16)
+def test_bf16_small_full(B, H, Sq, Skv, D, out_f32):
+    log(f"case: bf16 B{B} H{H} Sq{Sq} Skv{Skv} D{D} out_f32={out_f32}")
+    seed = 2000 + Sq * 7 + Skv + D
+    qb = inputs.random_bf16((B, H, Sq, D), seed)
+    kb = inputs.random_bf16((B, H, Skv, D), seed + 1)
+    vb = inputs.random_bf16((B, H, Skv, D), seed + 2)
+    o, lse = cp.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb),
+                         out_dtype=torch.float32 if out_f32 else None)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+    assert_bf16_parity(host64(o), host64(lse), O, L, "bf16 small")
+
+
+def test_bf16_closed_forms():
+    D, Sq, Skv = 128, 300, 700
+    qb = inputs.random_bf16((1, 2, Sq, D), 31)
+    vb = inputs.random_bf16((1, 2, Skv, D), 32)
+    # identical keys: O = mean of V exactly in real arithmetic; LSE = scale q.k + ln Skv
+    k1 = inputs.random_bf16((1, 2, 1, D), 33)
+    kb = np.repeat(k1, Skv, axis=2)
+    o, lse = cp.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb))
+    torch.cuda.synchronize()
+    V = f64_of_bf16(vb)
+    mean_v = np.broadcast_to(V.mean(axis=2, keepdims=True), (1, 2, Sq, D))
+    err = np.max(np.abs(host64(o) - mean_v))
+    L_ref = scale_of(D) * np.einsum("bhid,bhd->bhi", f64_of_bf16(qb), f64_of_bf16(k1)[:, :, 0]) + math.log(Skv)
+    lse_err = np.max(np.abs(host64(lse) - L_ref))
+    log(f"  identical keys: O vs mean(V) max-abs {err:.3e}; LSE {lse_err:.3e}")
+    assert err <= 4e-3 and lse_err <= 1e-3
+    # V = 1: O = 1
+    ones = inputs.f32_to_bf16_bits(np.ones((1, 2, Skv, D), np.float32))
+    o, _ = cp.attn_fwd(dev_bf16(qb), dev_bf16(inputs.random_bf16((1, 2, Skv, D), 34)), dev_bf16(ones))
+    torch.cuda.synchronize()
+    err = np.max(np.abs(host64(o) - 1.0))
+    log(f"  V = 1: max |O - 1| {err:.3e}")
+    assert err <= 8e-3
+
+
+def test_bf16_large_scores_stay_finite():
+    # |scores| up to ~50 and beyond: checks the running-max shift
+    D = 128
+    qb = inputs.random_bf16((1, 2, 256, D), 41, scale=8.0)
+    kb = inputs.random_bf16((1, 2, 500, D), 42)
+    vb = inputs.random_bf16((1, 2, 500, D), 43)
+    o, lse = cp.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+    og, lg = host64(o), host64(lse)
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
+    # sharp softmax: a single key dominates most rows, so O is close to one row of V
+    assert np.max(np.abs(og - O)) <= 3 * BF16_MAX_ABS
+    assert np.max(np.abs(lg - L)) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_keys(dtype):
+    D = 64
+    if dtype == "bf16":
+        q = dev_bf16(inputs.random_bf16((1, 2, 40, D), 51))
+        kv = torch.empty((1, 2, 0, D), dtype=torch.bfloat16, device="cuda")
+    else:
+        q = dev_f32(inputs.random_f32((1, 2, 40, D), 51))
+        kv = torch.empty((1, 2, 0, D), dtype=torch.float32, device="cuda")
+    o = torch.full(q.shape, 7.0, dtype=q.dtype, device="cuda")
+    lse = torch.zeros((1, 2, 40), device="cuda")
+    cp.attn_fwd(q, kv, kv, o=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_deterministic():
+    qb = inputs.random_bf16((1, 2, 700, 128), 61)
+    kb = inputs.random_bf16((1, 2, 900, 128), 62)
+    vb = inputs.random_bf16((1, 2, 900, 128), 63)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    o1, l1 = cp.attn_fwd(q, k, v)
+    o2, l2 = cp.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_rows_are_independent_of_tile_position():
+    """Query rows are computed independently: a row slice of a bigger query
+    gives bit-identical rows when its offset keeps the same in-tile position."""
+    qb = inputs.random_bf16((1, 1, 1024, 128), 71)
+    kb = inputs.random_bf16((1, 1, 500, 128), 72)
+    vb = inputs.random_bf16((1, 1, 500, 128), 73)
+    k, v = dev_bf16(kb), dev_bf16(vb)
+    o_full, l_full = cp.attn_fwd(dev_bf16(qb), k, v)
+    o_part, l_part = cp.attn_fwd(dev_bf16(np.ascontiguousarray(qb[:, :, 512:])), k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o_full[:, :, 512:].view(torch.int16), o_part.view(torch.int16))
+    assert torch.equal(l_full[:, :, 512:], l_part)

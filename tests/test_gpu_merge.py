@@ -1,0 +1,96 @@
+"""GPU parity of attn_merge and the ring driver against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import long_sequence_bidirectional_amd as cp
+from long_sequence_bidirectional_amd import inputs
+from helpers import (assert_bf16_parity, dev_bf16, dev_f32, f64_of_bf16, host64, log, scale_of)
+
+pytestmark = pytest.mark.gpu
+
+
+def _partials(seed, B=1, H=3, S=300, D=128, lse_spread=4.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    oa = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    ob = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    la = (rng.standard_normal((B, H, S)) * lse_spread + 8).astype(np.float32)
+    lb = (rng.standard_normal((B, H, S)) * lse_spread + 8).astype(np.float32)
+    return oa, la, ob, lb
+
+
+@pytest.mark.parametrize("D", [64, 128, 8, 200])
+def test_merge_f32(D):
+    log(f"case: merge f32 D{D}")
+    oa, la, ob, lb = _partials(1 + D, D=D)
+    # a few rows with one or both sides empty
+    la[0, 0, :3] = -np.inf
+    oa[0, 0, :3] = 0
+    lb[0, 1, 5:7] = -np.inf
+    ob[0, 1, 5:7] = 0
+    la[0, 2, 9] = lb[0, 2, 9] = -np.inf
+    oa[0, 2, 9] = ob[0, 2, 9] = 0
+    o, l = cp.attn_merge(dev_f32(oa), dev_f32(la), dev_f32(ob), dev_f32(lb))
+    torch.cuda.synchronize()
+    O, L = oracle.merge(oa, la, ob, lb)
+    og, lg = host64(o), host64(l)
+    assert np.array_equal(np.isneginf(lg), np.isneginf(L))
+    fin = np.isfinite(L)
+    assert np.max(np.abs(og - O)) <= 2e-6
+    assert np.max(np.abs(lg[fin] - L[fin])) <= 2e-6
+    assert np.all(og[0, 2, 9] == 0)
+
+
+def test_merge_bf16_and_in_place():
+    oa, la, ob, lb = _partials(7)
+    oab = inputs.f32_to_bf16_bits(oa)
+    obb = inputs.f32_to_bf16_bits(ob)
+    O, L = oracle.merge(f64_of_bf16(oab), la, f64_of_bf16(obb), lb)
+    ta, tla = dev_bf16(oab), dev_f32(la)
+    o, l = cp.attn_merge(ta, tla, dev_bf16(obb), dev_f32(lb))
+    # in place into the first operand
+    cp.attn_merge(ta, tla, dev_bf16(obb), dev_f32(lb), o_out=ta, lse_out=tla)
+    torch.cuda.synchronize()
+    for og, lg in ((host64(o), host64(l)), (host64(ta), host64(tla))):
+        # bf16 output rounding: |err| <= 2^-9 |O| + f32 noise
+        assert np.all(np.abs(og - O) <= np.abs(O) * 2.0 ** -8 + 1e-6)
+        assert np.max(np.abs(lg - L)) <= 2e-6
+    assert torch.equal(o.view(torch.int16), ta.view(torch.int16))
+
+
+def test_chunked_attention_merged_equals_unchunked():
+    D, Sq = 128, 400
+    qb = inputs.random_bf16((1, 2, Sq, D), 11)
+    kb = inputs.random_bf16((1, 2, 1100, D), 12)
+    vb = inputs.random_bf16((1, 2, 1100, D), 13)
+    q = dev_bf16(qb)
+    edges = [0, 300, 301, 700, 1100]
+    acc = None
+    for a, b in zip(edges[:-1], edges[1:]):
+        k = dev_bf16(np.ascontiguousarray(kb[:, :, a:b]))
+        v = dev_bf16(np.ascontiguousarray(vb[:, :, a:b]))
+        o, l = cp.attn_fwd(q, k, v, out_dtype=torch.float32)
+        acc = (o, l) if acc is None else cp.attn_merge(acc[0], acc[1], o, l, o_out=acc[0], lse_out=acc[1])
+    torch.cuda.synchronize()
+    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+    assert_bf16_parity(host64(acc[0]), host64(acc[1]), O, L, "4 chunks merged")
+
+
+@pytest.mark.parametrize("n,Skv_c,Sq", [(8, 200, 300), (3, 64, 65), (1, 100, 50), (4, 0, 20)])
+def test_ring_driver(n, Skv_c, Sq):
+    log(f"case: ring n{n} Skv_c{Skv_c} Sq{Sq}")
+    D, H = 128, 2
+    qb = inputs.random_bf16((1, H, Sq, D), 21)
+    kcb = inputs.random_bf16((n, 1, H, Skv_c, D), 22)
+    vcb = inputs.random_bf16((n, 1, H, Skv_c, D), 23)
+    o, l = cp.ring_attn_fwd(dev_bf16(qb), dev_bf16(kcb), dev_bf16(vcb))
+    torch.cuda.synchronize()
+    if Skv_c == 0:
+        assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+        return
+    # the chunks in order are the full key sequence
+    k_all = np.concatenate([kcb[c] for c in range(n)], axis=2)
+    v_all = np.concatenate([vcb[c] for c in range(n)], axis=2)
+    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(k_all), f64_of_bf16(v_all), scale_of(D))
+    assert_bf16_parity(host64(o), host64(l), O, L, "ring")
