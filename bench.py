@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark: per-rank attention of a context-parallel video diffusion transformer on one MI355X.
+
+One step = one denoising step's worth of attention on the full single-GPU
+video workload: 36 layers x (bf16 self-attention S=44160, H=24, D=128, plus
+cross-attention of the 44160 video queries to 2992 text keys), on seeded
+synthetic N(0,1) inputs resident in HBM before timing starts.  The workload
+models the Cosmos 3 setting described in "Simplifying model serving across
+multiple GPUs with NVIDIA TensorRT multi-device integration in NVIDIA
+Dynamo-Triton" (44160 video tokens, a 2992-token text path, 36 transformer
+layers); heads and head dim are assumed.
+
+Printed: one JSON line with the step throughput in TFLOP/s (4*B*H*Sq*Skv*D per
+attention call), the roofline of the dominant kernel (the self-attention
+launch, timed with HIP events on its own stream inside the timed region),
+the fp64 CPU oracle timed on a bounded row sample, and secondary
+measurements of the other kernels on the path (LSE merge, ring driver,
+Ulysses pack/unpack) at their per-rank shapes.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (256 CUs at 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+LAYERS = 36
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=LAYERS, help="attention layers per step (36 in the workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
+    ap.add_argument("--no-secondary", action="store_true", help="skip merge/ring/relayout measurements")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON file with rocprofv3 FETCH_SIZE/WRITE_SIZE per launch of the dominant kernel")
+    return ap.parse_args()
+
+
+def elapsed_ms(pairs):
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def cpu_baseline(budget_s: float):
+    """Time the fp64 oracle on a bounded sample of the self-attention workload.
+
+    Sample: blocks of 64 query rows of the S=44160 self-attention, head after
+    head, until the time budget is used; throughput = the sample's flops
+    (4 * rows * Skv * D) / seconds.
+    """
+    import numpy as np
+    import oracle
+    from long_sequence_bidirectional_amd import inputs
+
+    g = inputs.video_set()
+    D, S, H = inputs.HEAD_DIM, inputs.S_VIDEO, inputs.N_HEADS
+    scale = 1.0 / math.sqrt(D)
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = cores
+    rows_done, t_total, heads_used = 0, 0.0, 0
+    rng = np.random.Generator(np.random.PCG64(inputs.SEED))
+    for h in range(H):
+        if t_total >= budget_s:
+            break
+        k = inputs.bf16_bits_to_f32(g["k"][:, h:h + 1]).astype(np.float64)
+        v = inputs.bf16_bits_to_f32(g["v"][:, h:h + 1]).astype(np.float64)
+        heads_used += 1
+        while t_total < budget_s * (h + 1) / H:     # an equal share of the budget per head
+            r0 = int(rng.integers(0, S - 64))
+            q = inputs.bf16_bits_to_f32(g["q"][:, h:h + 1, r0:r0 + 64]).astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, scale)
+            t_total += time.perf_counter() - t0
+            rows_done += 64
+    flops = 4.0 * rows_done * S * D
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, blas_threads)),
+            "kind": "oracle",
+            "sample": f"{rows_done} query rows (blocks of 64) of the S=44160 H=24 D=128 self-attention "
+                      f"over {heads_used} heads, fp64 numpy, {t_total:.1f} s; host has {cores} cores"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import long_sequence_bidirectional_amd as cp
+    from long_sequence_bidirectional_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cp.lib()   # fail loudly now if the library is missing
+
+    D, S, H, S_TXT = inputs.HEAD_DIM, inputs.S_VIDEO, inputs.N_HEADS, inputs.S_TEXT
+    scale = 1.0 / math.sqrt(D)
+    g = inputs.video_set()
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, kt, vt = (dev(g[n]) for n in ("q", "k", "v", "k_text", "v_text"))
+    o_self = torch.empty_like(q)
+    l_self = torch.empty((1, H, S), dtype=torch.float32, device="cuda")
+    o_x = torch.empty_like(q)
+    l_x = torch.empty_like(l_self)
+    stream = torch.cuda.current_stream()
+
+    flops_self = 4.0 * H * S * S * D
+    flops_cross = 4.0 * H * S * S_TXT * D
+    flops_step = args.layers * (flops_self + flops_cross)
+
+    def step(ev_self=None):
+        for _ in range(args.layers):
+            if ev_self is not None:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            cp.attn_fwd(q, k, v, o=o_self, lse=l_self, scale=scale, stream=stream)
+            if ev_self is not None:
+                b.record(stream)
+                ev_self.append((a, b))
+            cp.attn_fwd(q, kt, vt, o=o_x, lse=l_x, scale=scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev_self = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step(ev_self)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    self_ms = elapsed_ms(ev_self)
+    self_avg = sum(self_ms) / len(self_ms)
+    achieved = flops_self / (self_avg * 1e-3) / 1e12
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("attn_fwd_bf16_self_bytes")
+
+    secondary = None if args.no_secondary else secondary_rows(cp, torch, q, k, v, stream)
+
+    result = {
+        "metric": "attention TFLOP/s (bf16) and % of MFMA peak at S=44160, H=24, D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16)",
+        "config": {"workload": "video_layer: 36 x (self-attention S=44160 + cross-attention to 2992 text "
+                               "tokens), H=24, D=128, B=1, non-causal",
+                   "B": 1, "H": H, "S": S, "S_text": S_TXT, "D": D, "layers": args.layers},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_bf16_kernel<128,8,false> (self-attention S=44160)",
+                     "avg_launch_ms": round(self_avg, 4), "launches": len(self_ms)},
+        "wall_s_timed": round(wall, 3),
+        "secondary": secondary,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def secondary_rows(cp, torch, q, k, v, stream):
+    """Timings of the other kernels on the path, at their per-rank shapes."""
+    from long_sequence_bidirectional_amd import inputs
+    S_L, P, H, D = inputs.S_LOCAL, inputs.CP_DEGREE, inputs.N_HEADS, inputs.HEAD_DIM
+    out = {}
+
+    def timeit(fn, iters=20):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    # ring_rank: Q 5520 rows vs 8 chunks of 5520 keys (8 attn_fwd with f32 partials + 7 merges)
+    q_l = q[:, :, :S_L].contiguous()
+    kc = torch.stack([k[:, :, c * S_L:(c + 1) * S_L] for c in range(P)]).contiguous()
+    vc = torch.stack([v[:, :, c * S_L:(c + 1) * S_L] for c in range(P)]).contiguous()
+    o = torch.empty((1, H, S_L, D), dtype=torch.float32, device="cuda")
+    l = torch.empty((1, H, S_L), dtype=torch.float32, device="cuda")
+    ow, lw = torch.empty_like(o), torch.empty_like(l)
+    ms = timeit(lambda: cp.ring_attn_fwd(q_l, kc, vc, o=o, lse=l, o_work=ow, lse_work=lw, stream=stream), 5)
+    out["ring_rank_tflops"] = round(4.0 * H * S_L * S_L * P * D / ms / 1e9, 1)
+    # allgather_kv_rank: Q 5520 vs K/V 44160
+    o_b = torch.empty((1, H, S_L, D), dtype=torch.bfloat16, device="cuda")
+    ms = timeit(lambda: cp.attn_fwd(q_l, k, v, o=o_b, lse=l, stream=stream), 5)
+    out["allgather_kv_rank_tflops"] = round(4.0 * H * S_L * inputs.S_VIDEO * D / ms / 1e9, 1)
+    # ulysses_rank attention: H=3, S=44160
+    q3, k3, v3 = (x[:, :3].contiguous() for x in (q, k, v))
+    o3 = torch.empty_like(q3)
+    l3 = torch.empty((1, 3, inputs.S_VIDEO), dtype=torch.float32, device="cuda")
+    ms = timeit(lambda: cp.attn_fwd(q3, k3, v3, o=o3, lse=l3, stream=stream), 5)
+    out["ulysses_rank_tflops"] = round(4.0 * 3 * inputs.S_VIDEO ** 2 * D / ms / 1e9, 1)
+    # merge (f32 O, the ring partial format): reads 2 O + 2 LSE, writes 1 O + 1 LSE
+    ms = timeit(lambda: cp.attn_merge(o, l, ow, lw, o_out=o, lse_out=l, stream=stream))
+    merge_bytes = 3 * o.numel() * 4 + 3 * l.numel() * 4
+    out["merge_f32_us"] = round(ms * 1e3, 2)
+    out["merge_f32_GBps"] = round(merge_bytes / ms / 1e6, 1)
+    # Ulysses relayout of a [5520, 24, 128] bf16 shard (33.9 MB read + written), hot in the 256 MB MALL
+    shard = q[0, :, :S_L].transpose(0, 1).contiguous().unsqueeze(0)
+    send = torch.empty((1, P, S_L, H // P, D), dtype=torch.bfloat16, device="cuda")
+    heads = torch.empty((1, H // P, S_L * P, D), dtype=torch.bfloat16, device="cuda")
+    nbytes = 2 * shard.numel() * 2
+    ms = timeit(lambda: cp.ulysses_pack(shard, P, cp.SEQ_TO_HEAD, dst=send, stream=stream))
+    out["pack_s2h_us"] = round(ms * 1e3, 2)
+    out["pack_s2h_GBps"] = round(nbytes / ms / 1e6, 1)
+    ms = timeit(lambda: cp.ulysses_unpack(send, P, cp.SEQ_TO_HEAD, dst=heads, stream=stream))
+    out["unpack_s2h_us"] = round(ms * 1e3, 2)
+    out["unpack_s2h_GBps"] = round(nbytes / ms / 1e6, 1)
+    return out
+
+
+if __name__ == "__main__":
+    main()
