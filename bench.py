@@ -188,7 +188,7 @@ def main():
                    "B": 1, "H": H, "S": S, "S_text": S_TXT, "D": D, "layers": args.layers},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_bf16_kernel<128,8,false> (self-attention S=44160)",
+                     "kernel": "attn_fwd_bf16_kernel<128,false> (self-attention S=44160)",
                      "avg_launch_ms": round(self_avg, 4), "launches": len(self_ms)},
         "wall_s_timed": round(wall, 3),
         "secondary": secondary,

@@ -20,7 +20,7 @@ ARCH = "gfx950"
 SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "merge.hip", "relayout.hip"]
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared", "-fvisibility=hidden",
     # No packed-fp32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

@@ -2,69 +2,110 @@
 //
 // Computes, per (b, h) and query row i, the online-softmax form of
 //   O_i = sum_j softmax_j(scale * q_i . k_j) v_j,   LSE_i = ln sum_j exp(scale * q_i . k_j)
-// streaming K/V in blocks of BN rows, as Ring Attention's blockwise online
+// streaming K/V in blocks of BN keys, as Ring Attention's blockwise online
 // softmax does ("Scaling AI inference across multiple GPUs using NVIDIA
 // TensorRT with multi-device inference support", section "Ring Attention";
 // no causal mask, section "Context parallelism").
 //
-// Work split.  One workgroup = NWAVES wave64s = one tile of BM = 32*NWAVES
-// query rows of one (b, h); wave w owns rows [32w, 32w+32) of the tile.
+// Work split.  One workgroup = 8 wave64s = one tile of 256 query rows of one
+// (b, h); wave w owns rows [32w, 32w+32) of the tile.
 //
 // Transposed formulation.  Each wave computes S^T = K Q^T and O^T = V^T P^T
 // with v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane
 // holds one column, so with queries on the column axis every lane owns one
-// query row: row max and row sum are lane-local apart from one exchange
-// between the two 32-lane halves, the softmax weights P^T come out of the
-// S^T accumulator already laid out as the B operand of the PV product (no
-// LDS round trip for P), and the rescale of O by exp(m_old - m_new) is a
-// per-lane scalar.
+// query row: the row max is lane-local apart from one exchange between the
+// two 32-lane halves, the row sum needs no exchange until the epilogue, the
+// softmax weights P^T come out of the S^T accumulator already laid out as the
+// B operand of the PV product (no LDS round trip for P), and the rescale of O
+// is a per-lane scalar.
 //
 //   S^T tile (32 keys x 32 queries):  lane l, register i holds
-//       key   (i/4)*8 + (l/32)*4 + i%4,  query l%32.
+//       key (i/4)*8 + (l/32)*4 + i%4,  query l%32.
 //   PV k-step t covers the 16 keys 16t..16t+15 of the block; lane half h
 //   supplies slots (h, 0..7) = S^T registers 8*(t%2)..+7 of key tile t/2,
-//   i.e. keys 16t + 8*(j/4) + 4h + j%4.  The V^T A-operand must use the same
-//   key order, so V is stored in LDS transposed with bits 2 and 3 of the key
-//   index swapped; each A fragment is then one 16-byte LDS read.
+//   i.e. keys 16t + 8*(j/4) + 4h + j%4.
 //
-// Staging.  K (row-major, padded) and V^T (padded) blocks live in LDS,
-// double-buffered: the global loads for block j+1 are issued before the
-// MFMAs of block j and written to the other buffer after them, with one
-// workgroup barrier per block.
+// LDS.  Q (256 x D, loaded once), K and V blocks (double-buffered) are stored
+// row-major with 16-byte chunks XOR-swizzled per row and filled by direct
+// global->LDS loads (global_load_lds_dwordx4: lane i writes bytes 16i..16i+15
+// of a 1 KB piece, so a wave's load is a plain copy and needs no registers).
+// The V^T A-operand of the PV product comes from two ds_read_b64_tr_b16 per
+// MFMA: in each 16-lane group, lane L points at row kv0 + L/4, columns
+// d0 + 4(L%4) .. +3 and receives V[kv0 .. kv0+3][d0 + L], i.e. four keys of
+// one head-dim column -- exactly the per-lane k-slots above.  The swizzles
+// make the K/Q reads (16 rows x one chunk) and the V transposing reads
+// (4 rows x 4 chunks) hit 64 distinct banks.
 //
-// Softmax in base 2: t = s * scale * log2(e); p = exp2(t - m); the natural
-// LSE is (m + log2 l) * ln 2.  Keys past Skv in the last block get -inf.
+// Schedule.  Per key block j a wave runs an MFMA slot M_j = {S_j = K_j Q^T,
+// O += V_{j-1} P_{j-1}} and a softmax slot SM_j (max, exp2, row sum, bf16
+// weights, rescale of O when needed).  Waves w and w+4 share a SIMD; group 1
+// (waves 4-7) runs one slot behind group 0, so on every SIMD one wave issues
+// MFMAs while the other computes exponentials, with one workgroup barrier
+// per slot.  In an MFMA slot the operand reads run four MFMAs ahead.
+//
+// Softmax in base 2: t = s * scale * log2(e), p = exp2(t - m), natural
+// LSE = (m + log2 l) * ln 2.  The running max m is only raised when a block's
+// max exceeds it by more than 2^8 (so p <= 256); otherwise the stale m is kept
+// and O needs no rescale.  The result is exact after the final division by l
+// because every term of O and l carries the same factor 2^-m.  Keys past Skv
+// in the last block get -inf.  Out-of-range rows are loaded clamped to the
+// last valid row (finite values that get weight 0 or are never stored).
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
+
+#define CPATTN_AI __attribute__((always_inline))
 
 namespace cpattn {
 namespace {
 
-constexpr int BN = 64;     // keys per block
-constexpr int KPAD = 8;    // bf16 pad per K row in LDS (keeps 16B reads conflict-free)
-constexpr int VPAD = 8;    // bf16 pad per V^T row in LDS
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T*)(p))
 
-__device__ __forceinline__ int swap_bits23(int x) {
-    return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+constexpr int kBM = 256;              // query rows per workgroup (8 waves x 32)
+constexpr int kBN = 64;               // keys per block
+constexpr int kReadAhead = 4;         // MFMA operand reads issued this many MFMAs ahead
+constexpr float kRescaleTh = 8.0f;    // raise m only when the block max exceeds it by > 2^8
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Chunk c of row r is stored at chunk position c ^ swz(r).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {     // K and Q: 16 consecutive rows, same chunk
+    constexpr int RPB = 256 / (2 * D);            // rows per 256-byte bank row
+    return (r / RPB) % (D / 8);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {     // V: 4 consecutive rows x 4 chunks
+    constexpr int RPB = 256 / (2 * D);
+    return 4 * ((r / RPB) % (D / 32));
 }
 
-template <int D, int NWAVES, bool OUT_F32>
-__global__ __launch_bounds__(NWAVES * 64) void attn_fwd_bf16_kernel(
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv, int nQt, int total_tiles,
-    int per_xcd, float c) {
-    constexpr int NT = NWAVES * 64;
-    constexpr int BM = NWAVES * 32;
-    constexpr int KSTR = D + KPAD;
-    constexpr int VSTR = BN + VPAD;
+    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv, int nQt, int total_tiles, int per_xcd,
+    float c) {
+    constexpr int BN = kBN;
+    constexpr int NC = D / 8;               // 16-byte chunks per row
     constexpr int NKS = D / 16;             // k-steps of the QK^T product
     constexpr int NDT = D / 32;             // 32-wide d tiles of O^T
-    constexpr int KCH = (BN * D / 8 + NT - 1) / NT;   // 16-byte K chunks per thread
-    constexpr int NVSB = (BN / 4) * (D / 4);          // 4x4 V sub-blocks per block
-    constexpr int VSB = (NVSB + NT - 1) / NT;         // sub-blocks per thread
+    constexpr int NKT = BN / 32;            // 32-key tiles of S^T per block
+    constexpr int NPB = BN / 16;            // 16-key k-steps of the PV product
+    constexpr int BLK_BYTES = BN * D * 2;
+    constexpr int LOADS_PER_WAVE = BLK_BYTES / 1024 / 8;
+    constexpr int ROWS_PER_LOAD = 1024 / (2 * D);
+    constexpr int Q_LOADS = 32 * D * 2 / 1024;
+    constexpr int NQK = NKT * NKS;          // MFMA jobs of S = K Q^T
+    constexpr int NPV = NDT * NPB;          // MFMA jobs of O += V^T P^T
+    static_assert(LOADS_PER_WAVE >= 1, "block too small for the loader");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs[kBM * D];
 
     // XCD-aware tile order: workgroup ids dealt round-robin over the XCDs are
     // mapped so that each XCD walks a contiguous range of tiles, i.e. the
@@ -80,145 +121,157 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_bf16_kernel(
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
+    const int L16 = lane & 15;
+    const int g16 = (lane >> 4) & 1;
+    const int group = wave >> 2;            // waves w and w+4 share a SIMD
 
     const uint16_t* qp = q + (size_t)bh * Sq * D;
     const uint16_t* kp = k + (size_t)bh * Skv * D;
     const uint16_t* vp = v + (size_t)bh * Skv * D;
-    const int qrow = qt * BM + wave * 32 + l32;
+    const int qrow = qt * kBM + wave * 32 + l32;
+    const int nblk = (Skv + BN - 1) / BN;
 
-    // Q^T fragments (B operand of S^T = K Q^T): query qrow, dims 16*ks + 8*hh .. +7.
-    u32x4 qf[NKS];
-    if (qrow < Sq) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(qp + (size_t)qrow * D);
+    // ---- direct global -> LDS loads (rows clamped to the last valid one)
+    auto load_rows = [&](const uint16_t* src, uint16_t* dst, int row0, int nvalid, int inst,
+                         bool is_v) CPATTN_AI {
+        const int row = inst * ROWS_PER_LOAD + lane / NC;
+        const int ch = (lane % NC) ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+        const int r = min(row0 + row, nvalid - 1);
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src + (size_t)r * D + ch * 8),
+                                         LDS_PTR(void, dst + inst * 512), 16, 0, 0);
+    };
+    auto load_block = [&](const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = src[2 * ks + hh];
-    } else {
+        for (int i = 0; i < LOADS_PER_WAVE; ++i)
+            load_rows(src, dst, j * BN, Skv, wave * LOADS_PER_WAVE + i, is_v);
+    };
+    auto wait_loads = [&]() CPATTN_AI { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+    // Q tile: this wave's 32 rows, swizzled like K.
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = u32x4{0, 0, 0, 0};
+    for (int i = 0; i < Q_LOADS; ++i) load_rows(qp, Qs, qt * kBM, Sq, wave * Q_LOADS + i, false);
+
+    // ---- LDS read addresses: lane-dependent parts (elements); the rest folds into offsets
+    int qoff[NKS], koff[NKS], voff[NDT];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        qoff[ks] = (wave * 32 + l32) * D + (((2 * ks + hh) ^ swz_k<D>(wave * 32 + l32)) * 8);
+        koff[ks] = l32 * D + (((2 * ks + hh) ^ swz_k<D>(l32)) * 8);
     }
-
-    u32x4 kreg[KCH];
-    u32x2 vreg[VSB][4];
-
-    auto load_block = [&](int j) {
-        const int kv0 = j * BN;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int ch = tid + i * NT;
-            const int row = ch / (D / 8);
-            const int c8 = ch - row * (D / 8);
-            const int kv = kv0 + row;
-            if (ch < BN * D / 8 && kv < Skv)
-                kreg[i] = reinterpret_cast<const u32x4*>(kp + (size_t)kv * D)[c8];
-            else
-                kreg[i] = u32x4{0, 0, 0, 0};
-        }
+    for (int dt = 0; dt < NDT; ++dt) {
+        const int col = dt * 32 + 16 * g16 + 4 * (L16 & 3);
+        const int row = 4 * hh + (L16 >> 2);
+        voff[dt] = row * D + (((col >> 3) ^ swz_v<D>(row)) * 8) + ((col >> 2) & 1) * 4;
+    }
+    auto read_k = [&]<int BUF>(ic<BUF>, int kt, int ks) CPATTN_AI -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(&Ks[BUF][kt * 32 * D + koff[ks]]);
+    };
+    auto read_vt = [&]<int BUF>(ic<BUF>, int dt, int t) CPATTN_AI -> u32x4 {
+        i16x4 r[2];
 #pragma unroll
-        for (int i = 0; i < VSB; ++i) {
-            const int sb = tid + i * NT;
-            const int dq = (sb & 7) + ((sb >> 3) / (BN / 4)) * 8;
-            const int kvq = (sb >> 3) % (BN / 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kv = kv0 + kvq * 4 + r;
-                if (sb < NVSB && kv < Skv)
-                    vreg[i][r] = reinterpret_cast<const u32x2*>(vp + (size_t)kv * D)[dq];
-                else
-                    vreg[i][r] = u32x2{0, 0};
-            }
-        }
+        for (int h2 = 0; h2 < 2; ++h2)
+            r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDS_PTR(i16x4, &Vs[BUF][(16 * t + 8 * h2) * D + voff[dt]]));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, r[0]), a1 = __builtin_bit_cast(u32x2, r[1]);
+        return u32x4{a0[0], a0[1], a1[0], a1[1]};
     };
 
-    auto store_block = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int ch = tid + i * NT;
-            const int row = ch / (D / 8);
-            const int c8 = ch - row * (D / 8);
-            if (ch < BN * D / 8)
-                *reinterpret_cast<u32x4*>(&Ks[buf][row * KSTR + c8 * 8]) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VSB; ++i) {
-            const int sb = tid + i * NT;
-            if (sb >= NVSB) continue;
-            const int dq = (sb & 7) + ((sb >> 3) / (BN / 4)) * 8;
-            const int kvq = (sb >> 3) % (BN / 4);
-            const int pos = swap_bits23(kvq * 4);
-            // vreg[i][r] = V[kv = 4*kvq + r][4*dq .. 4*dq+3] as two dwords (d pairs).
-            // Output for d = 4*dq + e: keys r = 0..3 -> two dwords (r0|r1<<16, r2|r3<<16).
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int w = e >> 1;
-                const bool hi = e & 1;
-                uint32_t a0 = vreg[i][0][w], a1 = vreg[i][1][w], a2 = vreg[i][2][w], a3 = vreg[i][3][w];
-                uint32_t lo_pair = hi ? ((a0 >> 16) | (a1 & 0xFFFF0000u)) : ((a0 & 0xFFFFu) | (a1 << 16));
-                uint32_t hi_pair = hi ? ((a2 >> 16) | (a3 & 0xFFFF0000u)) : ((a2 & 0xFFFFu) | (a3 << 16));
-                *reinterpret_cast<u32x2*>(&Vt[buf][(dq * 4 + e) * VSTR + pos]) = u32x2{lo_pair, hi_pair};
-            }
-        }
-    };
-
+    // ---- per-wave state
     f32x16 oacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-
+    f32x16 s[NKT];             // S_j^T
+    u32x4 pb[NPB];             // P_j^T as the B operand of the PV product
     float m_run = -INFINITY;   // running max, base-2 units (scale*log2e applied)
     float l_run = 0.f;         // this lane half's partial row sum
+    float alpha = 1.f;
 
-    const int nblk = (Skv + BN - 1) / BN;
-    load_block(0);
-    store_block(0);
-    __syncthreads();
-
-    for (int j = 0; j < nblk; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nblk) load_block(j + 1);
-
-        // ---- S^T = K Q^T for the 64 keys of this block (two 32-key tiles)
-        f32x16 s[2];
+    // MFMA slot body: the job list [QK jobs in (ks, kt) order] ++ [PV jobs in (t, dt)
+    // order] (consecutive jobs use different accumulators), operand reads kReadAhead
+    // jobs ahead, fenced so the compiler keeps that distance.
+    auto mfma_jobs = [&]<int KB, int VB, bool QK, bool PV>(ic<KB>, ic<VB>, std::bool_constant<QK>,
+                                                           std::bool_constant<PV>) CPATTN_AI {
+        constexpr int J0 = QK ? 0 : NQK;
+        constexpr int J1 = PV ? NQK + NPV : NQK;
+        constexpr int NJ = J1 - J0;
+        if constexpr (QK) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-            const uint16_t* krow = &Ks[buf][(kt * 32 + l32) * KSTR + hh * 8];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                u32x4 a = *reinterpret_cast<const u32x4*>(krow + ks * 16);
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                __builtin_bit_cast(bf16x8, qf[ks]),
-                                                                s[kt], 0, 0, 0);
-            }
+                for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
         }
-
-        // ---- mask keys past Skv (only the last block can have them)
-        if ((j + 1) * BN > Skv) {
+        u32x4 frag[NJ];
+        u32x4 qfr[NKS];
+        auto rd = [&]<int I>(ic<I>) CPATTN_AI {
+            constexpr int jid = J0 + I;
+            if constexpr (jid < NQK) {
+                constexpr int kt = jid % NKT, ks = jid / NKT;
+                frag[I] = read_k(ic<KB>{}, kt, ks);
+                if constexpr (kt == 0) qfr[ks] = *reinterpret_cast<const u32x4*>(&Qs[qoff[ks]]);
+            } else {
+                constexpr int p = jid - NQK;
+                frag[I] = read_vt(ic<VB>{}, p % NDT, p / NDT);
+            }
+        };
+        auto step = [&]<int I>(ic<I>) CPATTN_AI {
+            if constexpr (I + kReadAhead < NJ) rd(ic<I + kReadAhead>{});
+            constexpr int jid = J0 + I;
+            if constexpr (jid < NQK) {
+                constexpr int kt = jid % NKT, ks = jid / NKT;
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, frag[I]),
+                                                                __builtin_bit_cast(bf16x8, qfr[ks]), s[kt],
+                                                                0, 0, 0);
+            } else {
+                constexpr int p = jid - NQK, dt = p % NDT, t = p / NDT;
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, frag[I]),
+                                                                   __builtin_bit_cast(bf16x8, pb[t]), oacc[dt],
+                                                                   0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI {
+            (rd(ic<Is>{}), ...);
+        }(std::make_integer_sequence<int, (kReadAhead < NJ ? kReadAhead : NJ)>{});
+        __builtin_amdgcn_sched_barrier(0);
+        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI {
+            (step(ic<Is>{}), ...);
+        }(std::make_integer_sequence<int, NJ>{});
+    };
+    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1), with P = j & 1.
+    auto M = [&]<int P>(ic<P>, int j) CPATTN_AI {
+        __builtin_amdgcn_s_setprio(1);
+        if (j < nblk && j >= 1) mfma_jobs(ic<P>{}, ic<1 - P>{}, std::true_type{}, std::true_type{});
+        else if (j < nblk) mfma_jobs(ic<P>{}, ic<1 - P>{}, std::true_type{}, std::false_type{});
+        else if (j >= 1) mfma_jobs(ic<P>{}, ic<1 - P>{}, std::false_type{}, std::true_type{});
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // SM_j: softmax of S_j -> P_j, row statistics, O *= alpha_j when some row raised its max.
+    auto SM = [&](int j) CPATTN_AI {
+        if (j == nblk - 1 && (Skv % BN) != 0) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = j * BN + kt * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
                     if (key >= Skv) s[kt][i] = -INFINITY;
                 }
         }
-
-        // ---- online softmax (row = this lane's query)
         float mx = s[0][0];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-        mx = max_across_halves(mx);
-        const float m_new = fmaxf(m_run, mx * c);
-        const float alpha = exp2_fast(m_run - m_new);
+        mx = max_across_halves(mx) * c;
+        const bool raise = mx > m_run + kRescaleTh;
+        const float m_new = raise ? mx : m_run;
+        alpha = exp2_fast(m_run - m_new);   // 1 when not raised; 0 on the first block
         m_run = m_new;
-
         float psum = 0.f;
-        u32x4 pb[4];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 float p[8];
@@ -230,29 +283,57 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_bf16_kernel(
                 pb[kt * 2 + half] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
             }
-        }
         l_run = l_run * alpha + psum;
+        // keep the row sum and the packed weights materialised in this slot (otherwise
+        // the compiler defers them past the barrier and holds every weight live)
+        asm volatile("" : "+v"(l_run));
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int t = 0; t < NPB; ++t) asm volatile("" : "+v"(pb[t]));
+        if (__ballot(raise) != 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-
-        // ---- O^T += V^T P^T
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const uint16_t* vrow = &Vt[buf][(dt * 32 + l32) * VSTR + hh * 8];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                u32x4 a = *reinterpret_cast<const u32x4*>(vrow + t * 16);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                   __builtin_bit_cast(bf16x8, pb[t]),
-                                                                   oacc[dt], 0, 0, 0);
-            }
+                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
         }
+    };
+    // loads of K_{j+1} and V_j
+    auto issue = [&](int j) CPATTN_AI {
+        if (j + 1 < nblk) load_block(kp, Ks[(j + 1) & 1], j + 1, false);
+        if (j < nblk) load_block(vp, Vs[j & 1], j, true);
+    };
 
-        if (j + 1 < nblk) store_block(buf ^ 1);
+    load_block(kp, Ks[0], 0, false);
+    wait_loads();
+    __syncthreads();
+
+    // Both groups run M_0, SM_0, M_1, SM_1, ..., M_nblk; group 1 starts one slot late
+    // (an extra barrier up front; group 0 adds one at the end).  Global slot 2j starts
+    // the loads of (K_{j+1}, V_j); they are waited for before the barrier closing slot
+    // 2j+1, so they are in LDS for M_{j+1} (slot 2j+2) and overwrite only buffers whose
+    // last reader was M_{j-1} (slot 2j-1).
+    auto body = [&]<int P>(ic<P>, int j) CPATTN_AI {
+        if (group == 0) issue(j);
+        M(ic<P>{}, j);
+        if (group != 0) wait_loads();
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        if (group != 0) issue(j + 1);
+        if (j < nblk) SM(j);
+        if (group == 0) wait_loads();
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+    if (group != 0) {
+        issue(0);
         __syncthreads();
     }
+    int j = 0;
+    for (; j + 1 <= nblk; j += 2) {
+        body(ic<0>{}, j);
+        body(ic<1>{}, j + 1);
+    }
+    if (j <= nblk) body(ic<0>{}, j);
+    if (group == 0) __syncthreads();
 
     // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
     const float l_tot = sum_across_halves(l_run);
@@ -274,30 +355,29 @@ __global__ __launch_bounds__(NWAVES * 64) void attn_fwd_bf16_kernel(
                 }
             }
         if (hh == 0)
-            lse[(size_t)bh * Sq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+            lse[(size_t)bh * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 
-template <int D, int NWAVES, bool OUT_F32>
+template <int D, bool OUT_F32>
 hipError_t launch(const AttnFwdArgs& a) {
-    constexpr int BM = NWAVES * 32;
-    const int nQt = (int)((a.Sq + BM - 1) / BM);
+    const int nQt = (int)((a.Sq + kBM - 1) / kBM);
     const int64_t total = (int64_t)a.BH * nQt;
     const int per_xcd = (int)((total + kNumXcd - 1) / kNumXcd);
     const int grid = per_xcd * kNumXcd;
     const float c = (float)((double)a.scale * 1.4426950408889634);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NWAVES, OUT_F32>), dim3(grid), dim3(NWAVES * 64), 0,
-                       a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt,
-                       (int)total, per_xcd, c);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3(grid), dim3(512), 0, a.stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)total,
+                       per_xcd, c);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a) {
-    if (a.D == 128) return a.out_f32 ? launch<128, 8, true>(a) : launch<128, 8, false>(a);
-    return a.out_f32 ? launch<64, 8, true>(a) : launch<64, 8, false>(a);
+    if (a.D == 128) return a.out_f32 ? launch<128, true>(a) : launch<128, false>(a);
+    return a.out_f32 ? launch<64, true>(a) : launch<64, false>(a);
 }
 
 }  // namespace cpattn
