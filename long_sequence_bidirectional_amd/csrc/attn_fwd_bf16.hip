@@ -25,7 +25,7 @@
 //   supplies slots (h, 0..7) = S^T registers 8*(t%2)..+7 of key tile t/2,
 //   i.e. keys 16t + 8*(j/4) + 4h + j%4.
 //
-// LDS.  Q (256 x D, loaded once), K and V blocks (double-buffered) are stored
+// LDS.  Q (256 x D, loaded once), K and V blocks (three buffers each) are stored
 // row-major with 16-byte chunks XOR-swizzled per row and filled by direct
 // global->LDS loads (global_load_lds_dwordx4: lane i writes bytes 16i..16i+15
 // of a 1 KB piece, so a wave's load is a plain copy and needs no registers).
@@ -41,7 +41,10 @@
 // weights, rescale of O when needed).  Waves w and w+4 share a SIMD; group 1
 // (waves 4-7) runs one slot behind group 0, so on every SIMD one wave issues
 // MFMAs while the other computes exponentials, with one workgroup barrier
-// per slot.  In an MFMA slot the operand reads run four MFMAs ahead.
+// per slot.  In an MFMA slot the operand reads run six MFMAs ahead.  Global
+// loads are issued from softmax slots, two slots before their data is needed
+// (three K/V buffers), and the slot barriers are plain s_barrier: each wave
+// waits only for its own older loads (vmcnt) before arriving.
 //
 // Softmax in base 2: t = s * scale * log2(e), p = exp2(t - m), natural
 // LSE = (m + log2 l) * ln 2.  The running max m is only raised when a block's
@@ -66,7 +69,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;              // query rows per workgroup (8 waves x 32)
 constexpr int kBN = 64;               // keys per block
-constexpr int kReadAhead = 4;         // MFMA operand reads issued this many MFMAs ahead
+constexpr int kReadAhead = 6;         // MFMA operand reads issued this many MFMAs ahead
+constexpr int NBUF = 3;               // K and V buffers in LDS
 constexpr float kRescaleTh = 8.0f;    // raise m only when the block max exceeds it by > 2^8
 
 template <int I>
@@ -103,8 +107,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     constexpr int NPV = NDT * NPB;          // MFMA jobs of O += V^T P^T
     static_assert(LOADS_PER_WAVE >= 1, "block too small for the loader");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][BN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks[NBUF][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) uint16_t Qs[kBM * D];
 
     // XCD-aware tile order: workgroup ids dealt round-robin over the XCDs are
@@ -141,9 +145,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
                                          LDS_PTR(void, dst + inst * 512), 16, 0, 0);
     };
     auto load_block = [&](const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
-#pragma unroll
-        for (int i = 0; i < LOADS_PER_WAVE; ++i)
-            load_rows(src, dst, j * BN, Skv, wave * LOADS_PER_WAVE + i, is_v);
+        uint16_t* base = dst + wave * LOADS_PER_WAVE * 512;
+        auto one = [&]<int I>(ic<I>) CPATTN_AI {
+            const int row = (wave * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
+            const int ch = (lane % NC) ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+            const int r = min(j * BN + row, Skv - 1);
+            const char* g = reinterpret_cast<const char*>(src + (size_t)r * D + ch * 8) - I * 1024;
+            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, g), LDS_PTR(void, base), 16, I * 1024, 0);
+        };
+        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI { (one(ic<Is>{}), ...); }(
+            std::make_integer_sequence<int, LOADS_PER_WAVE>{});
     };
     auto wait_loads = [&]() CPATTN_AI { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -241,11 +252,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
         }(std::make_integer_sequence<int, NJ>{});
     };
     // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1), with P = j & 1.
-    auto M = [&]<int P>(ic<P>, int j) CPATTN_AI {
+    auto M = [&]<int R>(ic<R>, int j) CPATTN_AI {   // R = j % 3
+        constexpr int KB = R, VB = (R + 2) % 3;
         __builtin_amdgcn_s_setprio(1);
-        if (j < nblk && j >= 1) mfma_jobs(ic<P>{}, ic<1 - P>{}, std::true_type{}, std::true_type{});
-        else if (j < nblk) mfma_jobs(ic<P>{}, ic<1 - P>{}, std::true_type{}, std::false_type{});
-        else if (j >= 1) mfma_jobs(ic<P>{}, ic<1 - P>{}, std::false_type{}, std::true_type{});
+        if (j < nblk && j >= 1) mfma_jobs(ic<KB>{}, ic<VB>{}, std::true_type{}, std::true_type{});
+        else if (j < nblk) mfma_jobs(ic<KB>{}, ic<VB>{}, std::true_type{}, std::false_type{});
+        else if (j >= 1) mfma_jobs(ic<KB>{}, ic<VB>{}, std::false_type{}, std::true_type{});
         __builtin_amdgcn_s_setprio(0);
     };
     // SM_j: softmax of S_j -> P_j, row statistics, O *= alpha_j when some row raised its max.
@@ -296,44 +308,59 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
                 for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
         }
     };
-    // loads of K_{j+1} and V_j
-    auto issue = [&](int j) CPATTN_AI {
-        if (j + 1 < nblk) load_block(kp, Ks[(j + 1) & 1], j + 1, false);
-        if (j < nblk) load_block(vp, Vs[j & 1], j, true);
+    // loads issued at global slot 2j: K_{j+2} and V_{j+1} (into the buffers M_{j-1} released)
+    auto issue = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        if (j + 2 < nblk) load_block(kp, Ks[(R + 2) % 3], j + 2, false);
+        if (j + 1 < nblk) load_block(vp, Vs[(R + 1) % 3], j + 1, true);
+    };
+    // Wait until at most this wave's latest issue of loads (issue(jl)) is in flight.  The
+    // count is exact only when that issue was a full one (K and V); near the end, where it
+    // carried fewer loads, wait for everything.
+    auto wait_older = [&](int jl) CPATTN_AI {
+        if (jl + 2 < nblk)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS_PER_WAVE) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
     load_block(kp, Ks[0], 0, false);
+    if (nblk > 1) load_block(kp, Ks[1], 1, false);
+    load_block(vp, Vs[0], 0, true);
     wait_loads();
     __syncthreads();
 
-    // Both groups run M_0, SM_0, M_1, SM_1, ..., M_nblk; group 1 starts one slot late
-    // (an extra barrier up front; group 0 adds one at the end).  Global slot 2j starts
-    // the loads of (K_{j+1}, V_j); they are waited for before the barrier closing slot
-    // 2j+1, so they are in LDS for M_{j+1} (slot 2j+2) and overwrite only buffers whose
-    // last reader was M_{j-1} (slot 2j-1).
-    auto body = [&]<int P>(ic<P>, int j) CPATTN_AI {
-        if (group == 0) issue(j);
-        M(ic<P>{}, j);
-        if (group != 0) wait_loads();
+    // Both groups run M_0, SM_0, M_1, SM_1, ..., M_nblk; group 1 starts one slot late (an
+    // extra barrier up front; group 0 adds one at the end).  Each wave issues its share of
+    // (K_{j+2}, V_{j+1}) at the start of a softmax slot -- group 1 at global slot 2j, group 0
+    // at 2j+1 -- into the buffers last read by M_{j-1} (slots 2j-2, 2j-1).  Before the
+    // barrier ending a softmax slot a wave waits for all but its latest issue, so both
+    // shares are in LDS by the end of slot 2j+3, in time for M_{j+2} (slot 2j+4).  The slot
+    // barrier itself does not wait for outstanding memory operations.
+    auto slot_barrier = [&]() CPATTN_AI { asm volatile("s_barrier" ::: "memory"); };
+    auto body = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        M(ic<R>{}, j);
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        if (group != 0) issue(j + 1);
+        slot_barrier();
+        if (group != 0) issue(ic<(R + 1) % 3>{}, j + 1);
+        else issue(ic<R>{}, j);
         if (j < nblk) SM(j);
-        if (group == 0) wait_loads();
+        wait_older(group != 0 ? j + 1 : j);
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
+        slot_barrier();
     };
     if (group != 0) {
-        issue(0);
-        __syncthreads();
+        issue(ic<0>{}, 0);
+        slot_barrier();
     }
     int j = 0;
-    for (; j + 1 <= nblk; j += 2) {
+    for (; j + 2 <= nblk; j += 3) {
         body(ic<0>{}, j);
         body(ic<1>{}, j + 1);
+        body(ic<2>{}, j + 2);
     }
     if (j <= nblk) body(ic<0>{}, j);
-    if (group == 0) __syncthreads();
+    if (j + 1 <= nblk) body(ic<1>{}, j + 1);
+    if (group == 0) slot_barrier();
 
     // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
     const float l_tot = sum_across_halves(l_run);
