@@ -292,6 +292,56 @@ def secondary_rows(cp, torch, q, k, v, stream):
     ms = timeit(lambda: cp.ulysses_unpack(send, P, cp.SEQ_TO_HEAD, dst=heads, stream=stream))
     out["unpack_s2h_us"] = round(ms * 1e3, 2)
     out["unpack_s2h_GBps"] = round(nbytes / ms / 1e6, 1)
+    out.update(cold_rows(cp, torch, stream))
+    return out
+
+
+def cold_rows(cp, torch, stream, n_sets=12):
+    """Merge and relayout on rotating buffer sets larger than the 256 MB MALL, so every
+    call reads its inputs from HBM (reported beside the hot figures)."""
+    from long_sequence_bidirectional_amd import inputs
+    S_L, P, H, D = inputs.S_LOCAL, inputs.CP_DEGREE, inputs.N_HEADS, inputs.HEAD_DIM
+    out = {}
+
+    def rotate(fns):
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for f in fns:
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / len(fns)
+
+    # merge: n_sets x (o_a, o_b f32 [1,24,5520,128] + LSEs), in place into o_a: 814 MB of inputs
+    sets = []
+    for _ in range(n_sets):
+        oa = torch.randn((1, H, S_L, D), device="cuda")
+        la = torch.randn((1, H, S_L), device="cuda")
+        ob = torch.randn((1, H, S_L, D), device="cuda")
+        lb = torch.randn((1, H, S_L), device="cuda")
+        sets.append((oa, la, ob, lb))
+    fns = [lambda t=t: cp.attn_merge(t[0], t[1], t[2], t[3], o_out=t[0], lse_out=t[1], stream=stream) for t in sets]
+    ms = rotate(fns)
+    nbytes = 3 * sets[0][0].numel() * 4 + 3 * sets[0][1].numel() * 4
+    out["merge_f32_cold_us"] = round(ms * 1e3, 2)
+    out["merge_f32_cold_GBps"] = round(nbytes / ms / 1e6, 1)
+    del sets, fns
+    # relayout: n_sets x (shard [1,5520,24,128] bf16 -> send buffer): 814 MB touched
+    shards = [torch.randn((1, S_L, H, D), device="cuda").to(torch.bfloat16) for _ in range(n_sets)]
+    sends = [torch.empty((1, P, S_L, H // P, D), dtype=torch.bfloat16, device="cuda") for _ in range(n_sets)]
+    fns = [lambda a=a, b=b: cp.ulysses_pack(a, P, cp.SEQ_TO_HEAD, dst=b, stream=stream) for a, b in zip(shards, sends)]
+    ms = rotate(fns)
+    nbytes = 2 * shards[0].numel() * 2
+    out["pack_s2h_cold_us"] = round(ms * 1e3, 2)
+    out["pack_s2h_cold_GBps"] = round(nbytes / ms / 1e6, 1)
+    fns = [lambda a=a, b=b: cp.ulysses_unpack(b, P, cp.SEQ_TO_HEAD, dst=a.view(1, H // P, S_L * P, D), stream=stream)
+           for a, b in zip(shards, sends)]
+    ms = rotate(fns)
+    out["unpack_s2h_cold_us"] = round(ms * 1e3, 2)
+    out["unpack_s2h_cold_GBps"] = round(nbytes / ms / 1e6, 1)
     return out
 
 
