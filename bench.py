@@ -153,6 +153,9 @@ def main():
     o_x = torch.empty_like(q)
     l_x = torch.empty_like(l_self)
     stream = torch.cuda.current_stream()
+    # workspaces of the key-range split of each call's last, partial wave of tiles
+    ws_self = workspace(cp, torch, 1, H, S, S, D)
+    ws_x = workspace(cp, torch, 1, H, S, S_TXT, D)
 
     flops_self = 4.0 * H * S * S * D
     flops_cross = 4.0 * H * S * S_TXT * D
@@ -163,11 +166,11 @@ def main():
             if ev_self is not None:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-            cp.attn_fwd(q, k, v, o=o_self, lse=l_self, scale=scale, stream=stream)
+            cp.attn_fwd_ex(q, k, v, o=o_self, lse=l_self, scale=scale, workspace=ws_self, stream=stream)
             if ev_self is not None:
                 b.record(stream)
                 ev_self.append((a, b))
-            cp.attn_fwd(q, kt, vt, o=o_x, lse=l_x, scale=scale, stream=stream)
+            cp.attn_fwd_ex(q, kt, vt, o=o_x, lse=l_x, scale=scale, workspace=ws_x, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -213,8 +216,10 @@ def main():
                    "B": 1, "H": H, "S": S, "S_text": S_TXT, "D": D, "layers": args.layers},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_bf16_kernel<128,false> (self-attention S=44160)",
-                     "avg_launch_ms": round(self_avg, 4), "launches": len(self_ms)},
+                     "kernel": "attn_fwd_bf16_kernel<128,false> + merge_pieces_kernel<false> "
+                               "(self-attention S=44160; the events bracket both)",
+                     "avg_launch_ms": round(self_avg, 4), "launches": len(self_ms),
+                     "split": split_of(cp, H, S, S, D, ws_self)},
         "wall_s_timed": round(wall, 3),
         "secondary": secondary,
     }
@@ -225,11 +230,27 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def workspace(cp, torch, B, H, Sq, Skv, D):
+    n = cp.attn_fwd_workspace_size(B, H, Sq, Skv, D)
+    return torch.empty(n, dtype=torch.uint8, device="cuda")
+
+
+def split_of(cp, H, Sq, Skv, D, ws):
+    """The split plan attn_fwd_ex follows on this device for this workspace."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    slots = props.multi_processor_count   # one 160 KB-LDS workgroup per CU
+    tiles, pieces, nbytes = cp.attn_fwd_split_plan(1, H, Sq, Skv, D, slots, ws.numel())
+    return {"slots": slots, "tiles": H * -(-Sq // 256), "split_tiles": tiles, "pieces": pieces,
+            "workspace_bytes": nbytes}
+
+
 def profile_pass(cp, torch, q, k, v):
     """One self-attention launch and one copy of known size (counter calibration)."""
     o = torch.empty_like(q)
     l = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    cp.attn_fwd(q, k, v, o=o, lse=l)
+    B, H, S, D = q.shape
+    cp.attn_fwd_ex(q, k, v, o=o, lse=l, workspace=workspace(cp, torch, B, H, S, k.shape[2], D))
     shard = torch.empty(CALIB_SHAPE, dtype=torch.bfloat16, device="cuda").view(torch.int16).random_().view(
         torch.bfloat16)
     send = torch.empty((1, 8, CALIB_SHAPE[1], CALIB_SHAPE[2] // 8, CALIB_SHAPE[3]), dtype=torch.bfloat16,
@@ -257,25 +278,37 @@ def secondary_rows(cp, torch, q, k, v, stream):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / iters
 
-    # ring_rank: Q 5520 rows vs 8 chunks of 5520 keys (8 attn_fwd with f32 partials + 7 merges)
+    # ring_rank: Q 5520 rows vs 8 chunks of 5520 keys (chunk attention folded into the f32
+    # accumulator in its epilogue; the work buffers hold the split pieces)
     q_l = q[:, :, :S_L].contiguous()
     kc = torch.stack([k[:, :, c * S_L:(c + 1) * S_L] for c in range(P)]).contiguous()
     vc = torch.stack([v[:, :, c * S_L:(c + 1) * S_L] for c in range(P)]).contiguous()
     o = torch.empty((1, H, S_L, D), dtype=torch.float32, device="cuda")
     l = torch.empty((1, H, S_L), dtype=torch.float32, device="cuda")
     ow, lw = torch.empty_like(o), torch.empty_like(l)
+    ring_flops = 4.0 * H * S_L * S_L * P * D
     ms = timeit(lambda: cp.ring_attn_fwd(q_l, kc, vc, o=o, lse=l, o_work=ow, lse_work=lw, stream=stream), 5)
-    out["ring_rank_tflops"] = round(4.0 * H * S_L * S_L * P * D / ms / 1e9, 1)
+    out["ring_rank_tflops"] = round(ring_flops / ms / 1e9, 1)
+    ms = timeit(lambda: cp.ring_attn_fwd(q_l, kc, vc, o=o, lse=l, use_work=False, stream=stream), 5)
+    out["ring_rank_unsplit_tflops"] = round(ring_flops / ms / 1e9, 1)
     # allgather_kv_rank: Q 5520 vs K/V 44160
     o_b = torch.empty((1, H, S_L, D), dtype=torch.bfloat16, device="cuda")
+    ws = workspace(cp, torch, 1, H, S_L, inputs.S_VIDEO, D)
+    agkv_flops = 4.0 * H * S_L * inputs.S_VIDEO * D
+    ms = timeit(lambda: cp.attn_fwd_ex(q_l, k, v, o=o_b, lse=l, workspace=ws, stream=stream), 5)
+    out["allgather_kv_rank_tflops"] = round(agkv_flops / ms / 1e9, 1)
     ms = timeit(lambda: cp.attn_fwd(q_l, k, v, o=o_b, lse=l, stream=stream), 5)
-    out["allgather_kv_rank_tflops"] = round(4.0 * H * S_L * inputs.S_VIDEO * D / ms / 1e9, 1)
+    out["allgather_kv_rank_unsplit_tflops"] = round(agkv_flops / ms / 1e9, 1)
     # ulysses_rank attention: H=3, S=44160
     q3, k3, v3 = (x[:, :3].contiguous() for x in (q, k, v))
     o3 = torch.empty_like(q3)
     l3 = torch.empty((1, 3, inputs.S_VIDEO), dtype=torch.float32, device="cuda")
+    ws3 = workspace(cp, torch, 1, 3, inputs.S_VIDEO, inputs.S_VIDEO, D)
+    uly_flops = 4.0 * 3 * inputs.S_VIDEO ** 2 * D
+    ms = timeit(lambda: cp.attn_fwd_ex(q3, k3, v3, o=o3, lse=l3, workspace=ws3, stream=stream), 5)
+    out["ulysses_rank_tflops"] = round(uly_flops / ms / 1e9, 1)
     ms = timeit(lambda: cp.attn_fwd(q3, k3, v3, o=o3, lse=l3, stream=stream), 5)
-    out["ulysses_rank_tflops"] = round(4.0 * 3 * inputs.S_VIDEO ** 2 * D / ms / 1e9, 1)
+    out["ulysses_rank_unsplit_tflops"] = round(uly_flops / ms / 1e9, 1)
     # merge (f32 O, the ring partial format): reads 2 O + 2 LSE, writes 1 O + 1 LSE
     ms = timeit(lambda: cp.attn_merge(o, l, ow, lw, o_out=o, lse_out=l, stream=stream))
     merge_bytes = 3 * o.numel() * 4 + 3 * l.numel() * 4

@@ -1,6 +1,6 @@
 /*
  * cpattn -- per-rank attention for context-parallel diffusion transformers
- * on AMD Instinct MI355X (gfx950).  C ABI, version 1.
+ * on AMD Instinct MI355X (gfx950).  C ABI, version 2.
  *
  * What the library computes (sources are the pages' titles and sections):
  *
@@ -20,9 +20,15 @@
  *    sets into the result over their union -- the online-softmax step that
  *    lets Ring Attention stream K/V chunks (first page, "Ring Attention").
  *
+ *  - attn_fwd_ex: attn_fwd with a caller workspace (key-range split of the
+ *    last, partial wave of query tiles, folded back with the same merge) and
+ *    an accumulate mode that folds the result into an existing (O, LSE) --
+ *    one Ring Attention step with the merge done in the attention epilogue.
+ *
  *  - ring_attn_fwd: the per-rank ring loop on one device: attention of the
- *    local queries against each of n K/V chunks in turn, folded with
- *    attn_merge (first page, "Ring Attention").
+ *    local queries against each of n K/V chunks in turn, each chunk folded
+ *    into the running (O, LSE) by the attn_merge rule (first page, "Ring
+ *    Attention").
  *
  *  - ulysses_pack / ulysses_unpack: the sequence<->head relayout on either
  *    side of DeepSpeed Ulysses' two all-to-alls (first page, "DeepSpeed
@@ -35,8 +41,10 @@
  *
  *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous
  *    (row-major, last dimension fastest) and 16-byte aligned.  The library
- *    never allocates, frees or retains memory, keeps no state between calls
- *    and has no handles.
+ *    never allocates, frees or retains memory and has no handles; scratch
+ *    memory, where a call can use it, is a caller-owned workspace argument.
+ *    The only state kept between calls is a per-device cache of the number
+ *    of attention workgroups the device holds at once.
  *  - Work is enqueued on the caller's HIP stream (0 = the null stream) and
  *    runs asynchronously; the call returns once the launches are enqueued.
  *  - Argument checks run synchronously, on the host, before any HIP call.
@@ -61,7 +69,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 1
+#define CPATTN_ABI_VERSION 2
 
 typedef enum {
     CPATTN_OK = 0,
@@ -72,8 +80,12 @@ typedef enum {
     CPATTN_E_ALIGN = 5,    /* a pointer is not 16-byte aligned                    */
     CPATTN_E_ALIAS = 6,    /* buffers overlap where overlap is not allowed        */
     CPATTN_E_HIP = 7,      /* the HIP runtime rejected a launch                   */
-    CPATTN_E_SCALE = 8     /* the score scale is not a finite positive number     */
+    CPATTN_E_SCALE = 8,    /* the score scale is not a finite positive number     */
+    CPATTN_E_FLAGS = 9     /* unknown bits in a flags argument                    */
 } cpattn_status;
+
+/* Flags of cpattn_attn_fwd_ex. */
+#define CPATTN_FLAG_ACCUMULATE 1u
 
 typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
 
@@ -107,6 +119,63 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
                               hipStream_t stream);
 
 /*
+ * attn_fwd with a caller workspace and flags.
+ *
+ * Same tensors, dtypes, results and checks as cpattn_attn_fwd, plus:
+ *
+ *   workspace        device memory, 16-byte aligned, workspace_bytes long, or
+ *                    NULL with workspace_bytes = 0.  Contents on entry are
+ *                    ignored and undefined on return.  Must not overlap any
+ *                    tensor argument (CPATTN_E_ALIAS); NULL with a nonzero
+ *                    size is CPATTN_E_NULL.
+ *   flags            0 or CPATTN_FLAG_ACCUMULATE; other bits -> CPATTN_E_FLAGS.
+ *
+ * Workspace.  The bf16 kernel runs 256 query rows of one (b, h) per
+ * workgroup; when the tiles do not fill the device's last wave, the keys of
+ * the tiles in that wave are split into pieces that run in parallel, and a
+ * second kernel folds the pieces with the attn_merge rule.  The split is
+ * planned per call from the device's resident-workgroup count and limited
+ * to what the workspace holds: (D + 1) * 1024 bytes per piece.
+ * cpattn_attn_fwd_workspace_size gives the size the best plan uses;
+ * less (or none) only means fewer (or no) pieces.  f32 inputs never split.
+ * Results differ from cpattn_attn_fwd's only by f32 rounding in the fold.
+ *
+ * CPATTN_FLAG_ACCUMULATE.  (o, lse) hold on entry the result of attention
+ * over a disjoint key set (O normalised, f32; LSE natural; LSE = -inf with
+ * O = 0 for "nothing yet"), and on return the result over the union:
+ * each row is folded with the attn_merge rule in f32.  Requires in_dtype =
+ * BF16 and o_dtype = F32 (else CPATTN_E_DTYPE).  With Skv = 0 the call
+ * leaves (o, lse) unchanged.
+ */
+cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                 float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
+                                 uint32_t flags, void* workspace, uint64_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Workspace bytes cpattn_attn_fwd_ex uses for this problem on the CURRENT
+ * device (0 when no split helps, and for f32 inputs).  Makes HIP queries of
+ * the current device (CU count, kernel occupancy); CPATTN_E_HIP if they fail.
+ * Shape checks as for cpattn_attn_fwd (the scale is not needed).
+ */
+cpattn_status cpattn_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                             cpattn_dtype in_dtype, cpattn_dtype o_dtype,
+                                             uint64_t* bytes);
+
+/*
+ * The split plan of cpattn_attn_fwd_ex (bf16 inputs) for a device that holds
+ * `slots` attention workgroups at once, with workspace_bytes of workspace.
+ * Host only, no HIP call.  Outputs: split_tiles = number of trailing query
+ * tiles split (0 = no split), pieces = pieces per split tile (1 if none),
+ * bytes_used = workspace the plan uses.  slots = 0 means "unknown" (no
+ * split).  Shape checks as for cpattn_attn_fwd.
+ */
+cpattn_status cpattn_attn_fwd_split_plan(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                         int64_t slots, uint64_t workspace_bytes,
+                                         int64_t* split_tiles, int64_t* pieces, uint64_t* bytes_used);
+
+/*
  * Merge two partial attention results over disjoint key sets a and b.
  *
  *   o_a, o_b, o_out  [B, H, S, D]  o_dtype      lse_a, lse_b, lse_out  [B, H, S]  f32
@@ -133,14 +202,18 @@ cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_a, const void*
  *   k_chunks  [n_chunks, B, H, Skv_chunk, D]     bf16  (chunk c = the c-th block of keys
  *   v_chunks  [n_chunks, B, H, Skv_chunk, D]     bf16   a ring would deliver)
  *   o         [B, H, Sq, D]  f32 (output)          lse  [B, H, Sq] f32 (output)
- *   o_work    [B, H, Sq, D]  f32 (caller-owned scratch)
- *   lse_work  [B, H, Sq]     f32 (caller-owned scratch)
+ *   o_work    [B, H, Sq, D]  f32 (caller-owned scratch, or NULL)
+ *   lse_work  [B, H, Sq]     f32 (caller-owned scratch, or NULL; NULL exactly
+ *                                 when o_work is NULL, else CPATTN_E_NULL)
  *
  * Chunk 0's attention is written to (o, lse); every later chunk's attention
- * goes to (o_work, lse_work) and is merged into (o, lse) in place.  The
- * result equals attention over the concatenation of all chunks.  n_chunks
- * >= 1, Skv_chunk >= 0, D in {64, 128}, scale as for attn_fwd.  o, lse,
- * o_work and lse_work must not overlap each other or the inputs.
+ * is folded into (o, lse) in its epilogue with the attn_merge rule (f32), as
+ * cpattn_attn_fwd_ex with CPATTN_FLAG_ACCUMULATE does.  The work buffers, when
+ * given, serve as the workspace of the key-range split (contents undefined
+ * on return).  The result equals attention over the concatenation of all
+ * chunks.  n_chunks >= 1, Skv_chunk >= 0, D in {64, 128}, scale as for
+ * attn_fwd.  o, lse, o_work and lse_work must not overlap each other or the
+ * inputs.
  */
 cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_chunks, const void* v_chunks,
                                    float* o, float* lse, float* o_work, float* lse_work,

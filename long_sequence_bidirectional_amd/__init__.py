@@ -6,6 +6,9 @@ and calls the C ABI; all computation runs in the library's HIP kernels.
 torch provides device memory and streams.
 
   attn_fwd(q, k, v, o=None, lse=None, scale=None)        -> (o, lse)
+  attn_fwd_ex(q, k, v, o, lse, workspace=..., accumulate=False) -> (o, lse)
+  attn_fwd_workspace_size(B, H, Sq, Skv, D, ...)          -> bytes
+  attn_fwd_split_plan(B, H, Sq, Skv, D, slots, ws_bytes)  -> (split_tiles, pieces, bytes)
   attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None) -> (o_out, lse_out)
   ring_attn_fwd(q, k_chunks, v_chunks, ...)               -> (o, lse)
   ulysses_pack(src, P, direction, dst=None)               -> dst
@@ -13,11 +16,12 @@ torch provides device memory and streams.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
-from ._lib import (BF16, F32, HEAD_TO_SEQ, SEQ_TO_HEAD, CpattnError, check, lib)
+from ._lib import (BF16, F32, FLAG_ACCUMULATE, HEAD_TO_SEQ, SEQ_TO_HEAD, CpattnError, check, lib)
 
-__all__ = ["attn_fwd", "attn_merge", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
            "SEQ_TO_HEAD", "HEAD_TO_SEQ", "CpattnError", "lib"]
 
 
@@ -49,8 +53,7 @@ def _stream(stream):
     return s.cuda_stream
 
 
-def attn_fwd(q, k, v, o=None, lse=None, scale=None, out_dtype=None, stream=None):
-    """Non-causal attention with per-row LSE.  q [B,H,Sq,D], k/v [B,H,Skv,D]."""
+def _attn_operands(q, k, v, o, lse, scale, out_dtype):
     torch = _torch()
     B, H, Sq, D = q.shape
     Skv = k.shape[2]
@@ -66,11 +69,48 @@ def attn_fwd(q, k, v, o=None, lse=None, scale=None, out_dtype=None, stream=None)
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if o.shape != q.shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
         raise ValueError("o must be [B,H,Sq,D] and lse float32 [B,H,Sq]")
-    st = lib().cpattn_attn_fwd(_dev(q, "q"), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
-                               _dev(o, "o"), _dev(lse, "lse"), B, H, Sq, Skv, D, float(scale),
-                               _dtype_code(q), _dtype_code(o), _stream(stream))
-    check("cpattn_attn_fwd", st)
+    args = (_dev(q, "q"), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None, _dev(o, "o"),
+            _dev(lse, "lse"), B, H, Sq, Skv, D, float(scale), _dtype_code(q), _dtype_code(o))
+    return o, lse, args
+
+
+def attn_fwd(q, k, v, o=None, lse=None, scale=None, out_dtype=None, stream=None):
+    """Non-causal attention with per-row LSE.  q [B,H,Sq,D], k/v [B,H,Skv,D]."""
+    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype)
+    check("cpattn_attn_fwd", lib().cpattn_attn_fwd(*args, _stream(stream)))
     return o, lse
+
+
+def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, out_dtype=None, workspace=None, accumulate=False,
+                stream=None):
+    """attn_fwd with a workspace (uint8 device tensor, key-range split of the last wave) and an
+    accumulate mode that folds the result into the f32 (o, lse) already there."""
+    if accumulate and (o is None or lse is None):
+        raise ValueError("accumulate needs the existing o and lse")
+    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None and workspace.numel() > 0:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    flags = FLAG_ACCUMULATE if accumulate else 0
+    check("cpattn_attn_fwd_ex", lib().cpattn_attn_fwd_ex(*args, flags, ws_ptr, ws_bytes, _stream(stream)))
+    return o, lse
+
+
+def attn_fwd_workspace_size(B, H, Sq, Skv, D, in_dtype=BF16, o_dtype=BF16):
+    """Workspace bytes attn_fwd_ex uses for this problem on the current device."""
+    n = ctypes.c_uint64(0)
+    check("cpattn_attn_fwd_workspace_size",
+          lib().cpattn_attn_fwd_workspace_size(B, H, Sq, Skv, D, in_dtype, o_dtype, ctypes.byref(n)))
+    return n.value
+
+
+def attn_fwd_split_plan(B, H, Sq, Skv, D, slots, workspace_bytes=2**64 - 1):
+    """(split_tiles, pieces, bytes_used) of attn_fwd_ex on a device holding `slots` workgroups."""
+    t, p, b = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_uint64(0)
+    check("cpattn_attn_fwd_split_plan",
+          lib().cpattn_attn_fwd_split_plan(B, H, Sq, Skv, D, slots, workspace_bytes, ctypes.byref(t),
+                                           ctypes.byref(p), ctypes.byref(b)))
+    return t.value, p.value, b.value
 
 
 def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
@@ -98,7 +138,7 @@ def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
 
 
 def ring_attn_fwd(q, k_chunks, v_chunks, o=None, lse=None, o_work=None, lse_work=None, scale=None,
-                  stream=None):
+                  stream=None, use_work=True):
     """Ring attention over K/V chunks [n, B, H, Skv_chunk, D] (bf16); f32 O and LSE out."""
     torch = _torch()
     B, H, Sq, D = q.shape
@@ -112,13 +152,14 @@ def ring_attn_fwd(q, k_chunks, v_chunks, o=None, lse=None, o_work=None, lse_work
     dev = q.device
     o = o if o is not None else torch.empty((B, H, Sq, D), dtype=torch.float32, device=dev)
     lse = lse if lse is not None else torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
-    if n > 1:
-        o_work = o_work if o_work is not None else torch.empty_like(o)
-        lse_work = lse_work if lse_work is not None else torch.empty_like(lse)
+    if (o_work is None) != (lse_work is None):
+        raise ValueError("give both o_work and lse_work, or neither")
+    if o_work is None and use_work:   # scratch for the key-range split of partial waves
+        o_work, lse_work = torch.empty_like(o), torch.empty_like(lse)
     st = lib().cpattn_ring_attn_fwd(_dev(q, "q"), k_chunks.data_ptr() if Skv_c else None,
                                     v_chunks.data_ptr() if Skv_c else None, _dev(o, "o"), _dev(lse, "lse"),
-                                    _dev(o_work, "o_work") if n > 1 else None,
-                                    _dev(lse_work, "lse_work") if n > 1 else None,
+                                    _dev(o_work, "o_work") if o_work is not None else None,
+                                    _dev(lse_work, "lse_work") if lse_work is not None else None,
                                     B, H, Sq, Skv_c, n, D, float(scale), _stream(stream))
     check("cpattn_ring_attn_fwd", st)
     return o, lse

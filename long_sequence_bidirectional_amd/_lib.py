@@ -12,18 +12,25 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libcpattn.so")
 
 # enum values of include/cpattn.h
-OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_ALIGN, E_ALIAS, E_HIP, E_SCALE = range(9)
+OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_ALIGN, E_ALIAS, E_HIP, E_SCALE, E_FLAGS = range(10)
 BF16, F32 = 0, 1
 SEQ_TO_HEAD, HEAD_TO_SEQ = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
+FLAG_ACCUMULATE = 1
 
 STATUS_NAMES = {OK: "OK", E_NULL: "E_NULL", E_SHAPE: "E_SHAPE", E_DTYPE: "E_DTYPE", E_HEADDIM: "E_HEADDIM",
-                E_ALIGN: "E_ALIGN", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP", E_SCALE: "E_SCALE"}
+                E_ALIGN: "E_ALIGN", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP", E_SCALE: "E_SCALE",
+                E_FLAGS: "E_FLAGS"}
 
 # (name, restype, argtypes) of every exported function
 _P, _I64, _F, _E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+_U32, _U64 = ctypes.c_uint32, ctypes.c_uint64
+_PI64, _PU64 = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64)
 SIGNATURES = [
     ("cpattn_attn_fwd", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _P]),
+    ("cpattn_attn_fwd_ex", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _U32, _P, _U64, _P]),
+    ("cpattn_attn_fwd_workspace_size", _E, [_I64, _I64, _I64, _I64, _I64, _E, _E, _PU64]),
+    ("cpattn_attn_fwd_split_plan", _E, [_I64, _I64, _I64, _I64, _I64, _I64, _U64, _PI64, _PI64, _PU64]),
     ("cpattn_attn_merge", _E, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _E, _P]),
     ("cpattn_ring_attn_fwd", _E, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P]),
     ("cpattn_ulysses_pack", _E, [_P, _P, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),

@@ -3,6 +3,8 @@
 // include/cpattn.h.
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
 #include <initializer_list>
 #include <stdint.h>
 
@@ -81,13 +83,123 @@ cpattn_status check_attn_shapes(int64_t B, int64_t H, int64_t Sq, int64_t Skv, i
     return CPATTN_OK;
 }
 
+// ---- key-range split of the last, partial wave of tiles
+//
+// The bf16 kernel runs one tile (kAttnTileRows query rows of one (b, h)) per
+// workgroup, and `slots` workgroups are resident at once.  With T tiles the last
+// wave holds only T mod slots of them; splitting each of those tiles' keys into s
+// pieces gives the tail ceil(rem * s / slots) rounds of 1/s tile plus a fixed
+// cost per piece, which the planner minimises over s.
+constexpr int64_t kMinPieceBlocks = 4;      // key blocks (64 keys) per piece, at least
+constexpr double kPieceCostBlocks = 4.0;    // fixed cost of a piece, in key blocks
+constexpr int64_t kMaxPieces = 64;          // pieces per tile, at most
+
+struct SplitPlan {
+    int64_t tiles = 0, split_tiles = 0, pieces = 1;
+    uint64_t bytes = 0;   // workspace used
+};
+
+uint64_t piece_bytes(int64_t D) { return (uint64_t)cpattn::kAttnTileRows * (uint64_t)(D + 1) * 4u; }
+
+SplitPlan plan_split(int64_t BH, int64_t Sq, int64_t Skv, int64_t D, int64_t slots, uint64_t ws_bytes) {
+    SplitPlan p;
+    p.tiles = BH * ((Sq + cpattn::kAttnTileRows - 1) / cpattn::kAttnTileRows);
+    const int64_t nblk = (Skv + 63) / 64;
+    if (slots <= 0 || nblk < 2 * kMinPieceBlocks) return p;
+    const int64_t rem = p.tiles % slots;
+    if (rem == 0) return p;
+    const uint64_t max_pieces_ws = ws_bytes / piece_bytes(D);
+    const int64_t s_max = std::min<int64_t>(kMaxPieces, nblk / kMinPieceBlocks);
+    double best = 1.0;   // the unsplit tail: one round of whole tiles
+    int64_t best_s = 1;
+    for (int64_t s = 2; s <= s_max; ++s) {
+        if ((uint64_t)(rem * s) > max_pieces_ws) break;
+        const int64_t rounds = (rem * s + slots - 1) / slots;
+        const double cost = (double)rounds * (1.0 / (double)s + kPieceCostBlocks / (double)nblk);
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_s = s;
+        }
+    }
+    if (best_s == 1) return p;
+    p.split_tiles = rem;
+    p.pieces = best_s;
+    p.bytes = (uint64_t)(rem * best_s) * piece_bytes(D);
+    return p;
+}
+
+// Workgroups of the bf16 kernel resident at once on the current device (0 if unknown),
+// cached per device and output type.
+int64_t device_slots(int64_t D, bool out_f32) {
+    constexpr int kCachedDevices = 64;
+    static std::atomic<int64_t> cache[kCachedDevices][2][2];
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::atomic<int64_t>* slot =
+        (dev >= 0 && dev < kCachedDevices) ? &cache[dev][D == 128 ? 1 : 0][out_f32 ? 1 : 0] : nullptr;
+    if (slot) {
+        const int64_t v = slot->load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    const int64_t v = (int64_t)cus * cpattn::attn_fwd_bf16_blocks_per_cu(D, out_f32);
+    if (slot && v > 0) slot->store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// Attention of one K/V set into (o, lse): written, or folded into them when accumulate.
+// ws_o/ws_lse (capacity ws_pieces pieces each) hold the partials of a split; null = no split.
 cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t Sq,
                        int64_t Skv, int64_t D, float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
-                       hipStream_t stream) {
-    if (Skv == 0)
+                       bool accumulate, float* ws_o, float* ws_lse, int64_t ws_pieces, hipStream_t stream) {
+    if (Skv == 0) {   // empty key set: O = 0, LSE = -inf, the identity of the fold
+        if (accumulate) return CPATTN_OK;
         return hip_status(cpattn::launch_fill_empty(o, BH * Sq * D * dtype_size(o_dtype), lse, BH * Sq, stream));
-    cpattn::AttnFwdArgs a{q, k, v, o, lse, BH, Sq, Skv, D, scale, o_dtype == CPATTN_F32, stream};
-    return hip_status(in_dtype == CPATTN_BF16 ? cpattn::launch_attn_fwd_bf16(a) : cpattn::launch_attn_fwd_f32(a));
+    }
+    cpattn::AttnFwdArgs a{q, k, v, o, lse, BH, Sq, Skv, D, scale, o_dtype == CPATTN_F32, accumulate,
+                          0, 1, nullptr, nullptr, stream};
+    if (in_dtype != CPATTN_BF16) return hip_status(cpattn::launch_attn_fwd_f32(a));
+    if (ws_o && ws_lse && ws_pieces > 0) {
+        const SplitPlan p = plan_split(BH, Sq, Skv, D, device_slots(D, a.out_f32),
+                                       (uint64_t)ws_pieces * piece_bytes(D));
+        if (p.split_tiles > 0) {
+            a.split_tiles = p.split_tiles;
+            a.split_pieces = p.pieces;
+            a.ws_o = ws_o;
+            a.ws_lse = ws_lse;
+        }
+    }
+    return hip_status(cpattn::launch_attn_fwd_bf16(a));
+}
+
+struct AttnFwdCheck {
+    AttnCheck c;
+    Range rq, rk, rv, ro, rl;
+};
+
+// Checks shared by attn_fwd and attn_fwd_ex (everything but the workspace).
+cpattn_status check_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                             int64_t Sq, int64_t Skv, int64_t D, float scale, cpattn_dtype in_dtype,
+                             cpattn_dtype o_dtype, AttnFwdCheck* out) {
+    if (!q || !o || !lse || (Skv != 0 && (!k || !v))) return CPATTN_E_NULL;
+    if (!dtype_valid(in_dtype) || !dtype_valid(o_dtype)) return CPATTN_E_DTYPE;
+    if (in_dtype == CPATTN_F32 && o_dtype != CPATTN_F32) return CPATTN_E_DTYPE;
+    AttnCheck& c = out->c;
+    const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, scale, 32, &c);
+    if (st != CPATTN_OK) return st;
+    if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || (Skv && (!aligned16(k) || !aligned16(v))))
+        return CPATTN_E_ALIGN;
+    const int64_t isz = dtype_size(in_dtype), osz = dtype_size(o_dtype);
+    out->rq = range(q, c.q_elems * isz);
+    out->rk = range(k, c.kv_elems * isz);
+    out->rv = range(v, c.kv_elems * isz);
+    out->ro = range(o, c.q_elems * osz);
+    out->rl = range(lse, c.rows * 4);
+    const Range &rq = out->rq, &rk = out->rk, &rv = out->rv, &ro = out->ro, &rl = out->rl;
+    if (overlap(ro, rl) || overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) ||
+        overlap(rl, rk) || overlap(rl, rv))
+        return CPATTN_E_ALIAS;
+    return CPATTN_OK;
 }
 
 }  // namespace
@@ -95,21 +207,73 @@ cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, flo
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                             int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
                                             cpattn_dtype in_dtype, cpattn_dtype o_dtype, hipStream_t stream) {
-    if (!q || !o || !lse || (Skv != 0 && (!k || !v))) return CPATTN_E_NULL;
-    if (!dtype_valid(in_dtype) || !dtype_valid(o_dtype)) return CPATTN_E_DTYPE;
-    if (in_dtype == CPATTN_F32 && o_dtype != CPATTN_F32) return CPATTN_E_DTYPE;
-    AttnCheck c;
-    const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, scale, 32, &c);
+    AttnFwdCheck ck;
+    const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, &ck);
     if (st != CPATTN_OK) return st;
-    if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || (Skv && (!aligned16(k) || !aligned16(v))))
-        return CPATTN_E_ALIGN;
-    const int64_t isz = dtype_size(in_dtype), osz = dtype_size(o_dtype);
-    const Range rq = range(q, c.q_elems * isz), rk = range(k, c.kv_elems * isz), rv = range(v, c.kv_elems * isz);
-    const Range ro = range(o, c.q_elems * osz), rl = range(lse, c.rows * 4);
-    if (overlap(ro, rl) || overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) ||
-        overlap(rl, rk) || overlap(rl, rv))
-        return CPATTN_E_ALIAS;
-    return run_attn(q, k, v, o, lse, B * H, Sq, Skv, D, scale, in_dtype, o_dtype, stream);
+    return run_attn(q, k, v, o, lse, B * H, Sq, Skv, D, scale, in_dtype, o_dtype, false, nullptr, nullptr, 0,
+                    stream);
+}
+
+CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                                               int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                               float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
+                                               uint32_t flags, void* workspace, uint64_t workspace_bytes,
+                                               hipStream_t stream) {
+    if ((flags & ~(uint32_t)CPATTN_FLAG_ACCUMULATE) != 0) return CPATTN_E_FLAGS;
+    const bool acc = (flags & CPATTN_FLAG_ACCUMULATE) != 0;
+    AttnFwdCheck ck;
+    const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, &ck);
+    if (st != CPATTN_OK) return st;
+    if (acc && (in_dtype != CPATTN_BF16 || o_dtype != CPATTN_F32)) return CPATTN_E_DTYPE;
+    if (workspace_bytes != 0 && !workspace) return CPATTN_E_NULL;
+    int64_t ws_pieces = 0;
+    float *ws_o = nullptr, *ws_lse = nullptr;
+    if (workspace && workspace_bytes > 0) {
+        if (!aligned16(workspace)) return CPATTN_E_ALIGN;
+        if (workspace_bytes > (uint64_t)kMaxElems) return CPATTN_E_SHAPE;
+        const Range rw = range(workspace, (int64_t)workspace_bytes);
+        if (overlap(rw, ck.rq) || overlap(rw, ck.rk) || overlap(rw, ck.rv) || overlap(rw, ck.ro) ||
+            overlap(rw, ck.rl))
+            return CPATTN_E_ALIAS;
+        // layout: ws_o [pieces, tile rows, D] then ws_lse [pieces, tile rows]
+        ws_pieces = (int64_t)(workspace_bytes / piece_bytes(D));
+        ws_o = static_cast<float*>(workspace);
+        ws_lse = ws_o + (size_t)ws_pieces * cpattn::kAttnTileRows * D;
+    }
+    return run_attn(q, k, v, o, lse, B * H, Sq, Skv, D, scale, in_dtype, o_dtype, acc, ws_o, ws_lse, ws_pieces,
+                    stream);
+}
+
+CPATTN_EXPORT cpattn_status cpattn_attn_fwd_split_plan(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                                       int64_t slots, uint64_t workspace_bytes,
+                                                       int64_t* split_tiles, int64_t* pieces,
+                                                       uint64_t* bytes_used) {
+    if (!split_tiles || !pieces || !bytes_used) return CPATTN_E_NULL;
+    AttnCheck c;
+    const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, 1.0f, 32, &c);
+    if (st != CPATTN_OK) return st;
+    if (slots < 0 || slots > kMaxDim) return CPATTN_E_SHAPE;
+    const SplitPlan p = plan_split(B * H, Sq, Skv, D, slots, workspace_bytes);
+    *split_tiles = p.split_tiles;
+    *pieces = p.pieces;
+    *bytes_used = p.bytes;
+    return CPATTN_OK;
+}
+
+CPATTN_EXPORT cpattn_status cpattn_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                                           int64_t D, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
+                                                           uint64_t* bytes) {
+    if (!bytes) return CPATTN_E_NULL;
+    if (!dtype_valid(in_dtype) || !dtype_valid(o_dtype)) return CPATTN_E_DTYPE;
+    AttnCheck c;
+    const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, 1.0f, 32, &c);
+    if (st != CPATTN_OK) return st;
+    *bytes = 0;
+    if (in_dtype != CPATTN_BF16) return CPATTN_OK;
+    const int64_t slots = device_slots(D, o_dtype == CPATTN_F32);
+    if (slots <= 0) return CPATTN_E_HIP;
+    *bytes = plan_split(B * H, Sq, Skv, D, slots, UINT64_MAX).bytes;
+    return CPATTN_OK;
 }
 
 CPATTN_EXPORT cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
@@ -145,7 +309,7 @@ CPATTN_EXPORT cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_ch
     if (!q || !o || !lse) return CPATTN_E_NULL;
     if (n_chunks < 1 || n_chunks > kMaxDim) return CPATTN_E_SHAPE;
     if (Skv_chunk != 0 && (!k_chunks || !v_chunks)) return CPATTN_E_NULL;
-    if (n_chunks > 1 && (!o_work || !lse_work)) return CPATTN_E_NULL;
+    if ((o_work == nullptr) != (lse_work == nullptr)) return CPATTN_E_NULL;
     AttnCheck c;
     const cpattn_status st = check_attn_shapes(B, H, Sq, Skv_chunk, D, scale, 32, &c);
     if (st != CPATTN_OK) return st;
@@ -153,12 +317,12 @@ CPATTN_EXPORT cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_ch
     if (all_kv < 0) return CPATTN_E_SHAPE;
     if (!aligned16(q) || !aligned16(o) || !aligned16(lse) ||
         (Skv_chunk && (!aligned16(k_chunks) || !aligned16(v_chunks))) ||
-        (n_chunks > 1 && (!aligned16(o_work) || !aligned16(lse_work))))
+        (o_work && (!aligned16(o_work) || !aligned16(lse_work))))
         return CPATTN_E_ALIGN;
     const Range rq = range(q, c.q_elems * 2), rk = range(k_chunks, all_kv * 2), rv = range(v_chunks, all_kv * 2);
     const Range ro = range(o, c.q_elems * 4), rl = range(lse, c.rows * 4);
-    const Range rw = n_chunks > 1 ? range(o_work, c.q_elems * 4) : Range{0, 0};
-    const Range rlw = n_chunks > 1 ? range(lse_work, c.rows * 4) : Range{0, 0};
+    const Range rw = o_work ? range(o_work, c.q_elems * 4) : Range{0, 0};
+    const Range rlw = o_work ? range(lse_work, c.rows * 4) : Range{0, 0};
     const Range outs[4] = {ro, rl, rw, rlw};
     for (int i = 0; i < 4; ++i) {
         if (overlap(outs[i], rq) || overlap(outs[i], rk) || overlap(outs[i], rv)) return CPATTN_E_ALIAS;
@@ -167,15 +331,14 @@ CPATTN_EXPORT cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_ch
     }
     const int64_t BH = B * H;
     const int64_t chunk_bytes = c.kv_elems * 2;
-    cpattn_status s = run_attn(q, k_chunks, v_chunks, o, lse, BH, Sq, Skv_chunk, D, scale, CPATTN_BF16,
-                               CPATTN_F32, stream);
-    for (int64_t ch = 1; ch < n_chunks && s == CPATTN_OK; ++ch) {
+    // o_work / lse_work hold the key-range pieces of split tiles (one tile of rows each)
+    const int64_t ws_pieces = (o_work && lse_work) ? c.rows / cpattn::kAttnTileRows : 0;
+    cpattn_status s = CPATTN_OK;
+    for (int64_t ch = 0; ch < n_chunks && s == CPATTN_OK; ++ch) {
         const char* kc = static_cast<const char*>(k_chunks) + ch * chunk_bytes;
         const char* vc = static_cast<const char*>(v_chunks) + ch * chunk_bytes;
-        s = run_attn(q, kc, vc, o_work, lse_work, BH, Sq, Skv_chunk, D, scale, CPATTN_BF16, CPATTN_F32, stream);
-        if (s != CPATTN_OK) break;
-        cpattn::MergeArgs m{o, lse, o_work, lse_work, o, lse, c.rows, D, true, stream};
-        s = hip_status(cpattn::launch_attn_merge(m));
+        s = run_attn(q, kc, vc, o, lse, BH, Sq, Skv_chunk, D, scale, CPATTN_BF16, CPATTN_F32, ch > 0, o_work,
+                     lse_work, ws_pieces, stream);
     }
     return s;
 }
@@ -227,6 +390,7 @@ CPATTN_EXPORT const char* cpattn_status_string(cpattn_status s) {
         case CPATTN_E_ALIAS: return "buffers overlap where overlap is not allowed";
         case CPATTN_E_HIP: return "the HIP runtime rejected a launch";
         case CPATTN_E_SCALE: return "the score scale is not a finite positive number";
+        case CPATTN_E_FLAGS: return "unknown flag bits";
     }
     return "unknown status";
 }

@@ -67,7 +67,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 #define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T*)(p))
 
-constexpr int kBM = 256;              // query rows per workgroup (8 waves x 32)
+constexpr int kBM = kAttnTileRows;    // query rows per workgroup (8 waves x 32)
 constexpr int kBN = 64;               // keys per block
 constexpr int kReadAhead = 6;         // MFMA operand reads issued this many MFMAs ahead
 constexpr int NBUF = 3;               // K and V buffers in LDS
@@ -91,8 +91,7 @@ __device__ __forceinline__ int swz_v(int r) {     // V: 4 consecutive rows x 4 c
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv, int nQt, int total_tiles, int per_xcd,
-    float c) {
+    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, AttnTileMap map, float c) {
     constexpr int BN = kBN;
     constexpr int NC = D / 8;               // 16-byte chunks per row
     constexpr int NKS = D / 16;             // k-steps of the QK^T product
@@ -111,14 +110,35 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t Vs[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) uint16_t Qs[kBM * D];
 
-    // XCD-aware tile order: workgroup ids dealt round-robin over the XCDs are
-    // mapped so that each XCD walks a contiguous range of tiles, i.e. the
-    // workgroups resident on one XCD share a head and its K/V stream in L2.
+    // Work unit of this workgroup.  Workgroup ids are dealt round-robin over the
+    // XCDs; both parts of the grid are mapped so that each XCD walks a contiguous
+    // range of units, i.e. the workgroups resident on one XCD share a head and
+    // its K/V stream in L2.  Ids below grid_dp run whole tiles [0, n_dp); the
+    // rest run key-range pieces of tiles [n_dp, n_dp + n_split), piece-major so
+    // that neighbours read the same keys.  A piece p of s covers key blocks
+    // [p*nblk/s, (p+1)*nblk/s) and leaves a normalised f32 partial and its LSE
+    // in workspace slot (tile - n_dp) * s + p.
     const int bid = blockIdx.x;
-    const int logical = (bid % kNumXcd) * per_xcd + bid / kNumXcd;
-    if (logical >= total_tiles) return;
-    const int bh = logical / nQt;
-    const int qt = logical - bh * nQt;
+    const int nblk_all = (Skv_all + BN - 1) / BN;
+    int tile, kb0 = 0, slot = -1, nblk = nblk_all;
+    if (bid < map.grid_dp) {
+        const int logical = (bid % kNumXcd) * map.per_xcd_dp + bid / kNumXcd;
+        if (logical >= map.n_dp) return;
+        tile = logical;
+    } else {
+        const int u = bid - map.grid_dp;
+        const int logical = (u % kNumXcd) * map.per_xcd_sp + u / kNumXcd;
+        if (logical >= map.n_split * map.split_s) return;
+        const int p = logical / map.n_split;
+        const int ti = logical - p * map.n_split;
+        tile = map.n_dp + ti;
+        slot = ti * map.split_s + p;
+        kb0 = (int)((int64_t)p * nblk_all / map.split_s);
+        nblk = (int)((int64_t)(p + 1) * nblk_all / map.split_s) - kb0;
+    }
+    const int Skv = min(Skv_all - kb0 * BN, nblk * BN);   // keys of this unit
+    const int bh = tile / nQt;
+    const int qt = tile - bh * nQt;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -130,10 +150,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const int group = wave >> 2;            // waves w and w+4 share a SIMD
 
     const uint16_t* qp = q + (size_t)bh * Sq * D;
-    const uint16_t* kp = k + (size_t)bh * Skv * D;
-    const uint16_t* vp = v + (size_t)bh * Skv * D;
+    const uint16_t* kp = k + ((size_t)bh * Skv_all + (size_t)kb0 * BN) * D;
+    const uint16_t* vp = v + ((size_t)bh * Skv_all + (size_t)kb0 * BN) * D;
     const int qrow = qt * kBM + wave * 32 + l32;
-    const int nblk = (Skv + BN - 1) / BN;
 
     // ---- direct global -> LDS loads (rows clamped to the last valid one)
     auto load_rows = [&](const uint16_t* src, uint16_t* dst, int row0, int nvalid, int inst,
@@ -362,27 +381,56 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     if (j + 1 <= nblk) body(ic<1>{}, j + 1);
     if (group == 0) slot_barrier();
 
-    // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2
+    // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2; a piece goes to the workspace, an
+    // accumulating call folds the result into the (O, LSE) already in o/lse.
     const float l_tot = sum_across_halves(l_run);
-    if (qrow < Sq) {
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        const size_t orow = ((size_t)bh * Sq + qrow) * D;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const float lse_new = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (slot >= 0) {
+        const size_t wrow = (size_t)slot * kBM + wave * 32 + l32;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d0 = dt * 32 + g * 8 + hh * 4;
-                const float x0 = oacc[dt][g * 4 + 0] * inv, x1 = oacc[dt][g * 4 + 1] * inv;
-                const float x2 = oacc[dt][g * 4 + 2] * inv, x3 = oacc[dt][g * 4 + 3] * inv;
+                *reinterpret_cast<f32x4*>(map.ws_o + wrow * D + d0) =
+                    f32x4{oacc[dt][g * 4 + 0] * inv, oacc[dt][g * 4 + 1] * inv, oacc[dt][g * 4 + 2] * inv,
+                          oacc[dt][g * 4 + 3] * inv};
+            }
+        if (hh == 0) map.ws_lse[wrow] = lse_new;
+    } else if (qrow < Sq) {
+        const size_t orow = ((size_t)bh * Sq + qrow) * D;
+        float wa = 0.f, wb = inv, L = lse_new;   // O = wa * O_old + wb * acc
+        if (OUT_F32 && map.accumulate) {
+            const float la = lse[(size_t)bh * Sq + qrow];
+            const float mx = fmaxf(la, lse_new);
+            wb = 0.f;
+            L = -INFINITY;
+            if (mx != -INFINITY) {
+                const float ea = expf(la - mx), eb = expf(lse_new - mx);
+                const float tot = ea + eb;
+                L = mx + logf(tot);
+                wa = ea / tot;
+                wb = eb / tot * inv;
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + g * 8 + hh * 4;
+                f32x4 x = f32x4{oacc[dt][g * 4 + 0], oacc[dt][g * 4 + 1], oacc[dt][g * 4 + 2],
+                                oacc[dt][g * 4 + 3]} * wb;
                 if constexpr (OUT_F32) {
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = f32x4{x0, x1, x2, x3};
+                    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0);
+                    if (map.accumulate) x += *dst * wa;
+                    *dst = x;
                 } else {
                     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + d0) =
-                        u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+                        u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
                 }
             }
-        if (hh == 0)
-            lse[(size_t)bh * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        if (hh == 0) lse[(size_t)bh * Sq + qrow] = L;
     }
 }
 
@@ -390,14 +438,34 @@ template <int D, bool OUT_F32>
 hipError_t launch(const AttnFwdArgs& a) {
     const int nQt = (int)((a.Sq + kBM - 1) / kBM);
     const int64_t total = (int64_t)a.BH * nQt;
-    const int per_xcd = (int)((total + kNumXcd - 1) / kNumXcd);
-    const int grid = per_xcd * kNumXcd;
+    AttnTileMap m{};
+    m.n_dp = (int)(total - a.split_tiles);
+    m.per_xcd_dp = (m.n_dp + kNumXcd - 1) / kNumXcd;
+    m.grid_dp = m.per_xcd_dp * kNumXcd;
+    m.n_split = (int)a.split_tiles;
+    m.split_s = a.split_tiles > 0 ? (int)a.split_pieces : 1;
+    m.per_xcd_sp = (m.n_split * m.split_s + kNumXcd - 1) / kNumXcd;
+    m.ws_o = a.ws_o;
+    m.ws_lse = a.ws_lse;
+    m.accumulate = a.accumulate ? 1 : 0;
+    const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;
     const float c = (float)((double)a.scale * 1.4426950408889634);
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3(grid), dim3(512), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)total,
-                       per_xcd, c);
-    return hipGetLastError();
+                       static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, m, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.split_tiles == 0) return e;
+    MergePiecesArgs f{a.ws_o, a.ws_lse, a.o, a.lse, m.n_dp, m.n_split, m.split_s, nQt, a.Sq, a.D, a.out_f32,
+                      a.accumulate, a.stream};
+    return launch_merge_pieces(f);
+}
+
+template <int D, bool OUT_F32>
+int occupancy() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<D, OUT_F32>, 512, 0) != hipSuccess)
+        return 0;
+    return n;
 }
 
 }  // namespace
@@ -405,6 +473,11 @@ hipError_t launch(const AttnFwdArgs& a) {
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a) {
     if (a.D == 128) return a.out_f32 ? launch<128, true>(a) : launch<128, false>(a);
     return a.out_f32 ? launch<64, true>(a) : launch<64, false>(a);
+}
+
+int attn_fwd_bf16_blocks_per_cu(int64_t D, bool out_f32) {
+    if (D == 128) return out_f32 ? occupancy<128, true>() : occupancy<128, false>();
+    return out_f32 ? occupancy<64, true>() : occupancy<64, false>();
 }
 
 }  // namespace cpattn

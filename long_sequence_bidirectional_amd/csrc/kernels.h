@@ -7,6 +7,9 @@
 
 namespace cpattn {
 
+// Query rows per workgroup tile of the bf16 attention kernel.
+constexpr int kAttnTileRows = 256;
+
 struct AttnFwdArgs {
     const void* q;
     const void* k;
@@ -19,11 +22,52 @@ struct AttnFwdArgs {
     int64_t D;       // 64 or 128
     float scale;
     bool out_f32;
+    bool accumulate;       // fold into the (O, LSE) already in o/lse (out_f32 only)
+    // Key-range split of the last split_tiles tiles into split_pieces pieces each
+    // (bf16 kernel only; 0 = none).  Partials go to ws_o [split_tiles * split_pieces,
+    // kAttnTileRows, D] and ws_lse [split_tiles * split_pieces, kAttnTileRows] (f32) and
+    // are merged into o/lse by launch_merge_pieces.
+    int64_t split_tiles;
+    int64_t split_pieces;
+    float* ws_o;
+    float* ws_lse;
     hipStream_t stream;
+};
+
+// Kernel-side form of the work split (passed by value).
+struct AttnTileMap {
+    int n_dp, per_xcd_dp, grid_dp;      // whole tiles [0, n_dp)
+    int n_split, split_s, per_xcd_sp;   // split tiles [n_dp, n_dp + n_split), split_s pieces each
+    float* ws_o;
+    float* ws_lse;
+    int accumulate;
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a);
+
+// Resident workgroups per CU of the bf16 attention kernel (0 if the runtime cannot tell).
+int attn_fwd_bf16_blocks_per_cu(int64_t D, bool out_f32);
+
+// Merge of the key-range pieces of split tiles (and, when accumulating, of the
+// (O, LSE) already in o/lse) into the final rows of o/lse.
+struct MergePiecesArgs {
+    const float* ws_o;
+    const float* ws_lse;
+    void* o;
+    float* lse;
+    int first_tile;   // tile index of split tile 0
+    int n_split;
+    int pieces;
+    int nQt;          // tiles per (b, h)
+    int64_t Sq;
+    int64_t D;
+    bool out_f32;
+    bool accumulate;
+    hipStream_t stream;
+};
+
+hipError_t launch_merge_pieces(const MergePiecesArgs& a);
 
 // O = 0 (n_o elements of elem_bytes each), LSE = -inf (n_rows floats).
 hipError_t launch_fill_empty(void* o, int64_t o_bytes, float* lse, int64_t n_rows, hipStream_t stream);

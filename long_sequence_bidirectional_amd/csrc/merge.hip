@@ -128,6 +128,53 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const void* o_a, c
     if (lane == 0) lse_out[row] = L;
 }
 
+// Merge of the key-range pieces of split attention tiles.  The same fold over n
+// partials: M = max_p L_p, L = M + ln sum_p e^(L_p - M), O = sum_p e^(L_p - L) O_p,
+// where the partials are the tile's pieces (normalised f32 O, natural LSE) and,
+// when accumulating, the (O, LSE) already in o/lse.  One row per D/4 lanes, four
+// elements per lane.
+template <bool F32>
+__global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restrict__ ws_o,
+                                                           const float* __restrict__ ws_lse, void* o, float* lse,
+                                                           int first_tile, int n_split, int pieces, int nQt,
+                                                           int64_t Sq, int D, int accumulate) {
+    constexpr int TR = kAttnTileRows;
+    const int lpr = D >> 2;                       // lanes per row
+    const int64_t grow = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / lpr;
+    const int c4 = ((int)threadIdx.x % lpr) * 4;
+    const int ti = (int)(grow / TR);
+    const int r = (int)(grow - (int64_t)ti * TR);
+    if (ti >= n_split) return;
+    const int tile = first_tile + ti;
+    const int bh = tile / nQt;
+    const int64_t qrow = (int64_t)(tile - bh * nQt) * TR + r;
+    if (qrow >= Sq) return;
+    const size_t row = (size_t)bh * Sq + qrow;
+    const float* lp = ws_lse + (size_t)ti * pieces * TR + r;
+    const float* op = ws_o + ((size_t)ti * pieces * TR + r) * D + c4;
+    const float la = accumulate ? lse[row] : -INFINITY;
+    float mx = la;
+    for (int p = 0; p < pieces; ++p) mx = fmaxf(mx, lp[(size_t)p * TR]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float L = -INFINITY;
+    if (mx != -INFINITY) {
+        float tot = expf(la - mx);
+        for (int p = 0; p < pieces; ++p) tot += expf(lp[(size_t)p * TR] - mx);
+        L = mx + logf(tot);
+        if (accumulate) acc = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + row * D + c4) *
+                              expf(la - L);
+        for (int p = 0; p < pieces; ++p)
+            acc += *reinterpret_cast<const f32x4*>(op + (size_t)p * TR * D) * expf(lp[(size_t)p * TR] - L);
+    }
+    if constexpr (F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + row * D + c4) = acc;
+    } else {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + row * D + c4) =
+            u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    }
+    if (c4 == 0) lse[row] = L;
+}
+
 }  // namespace
 
 hipError_t launch_attn_merge(const MergeArgs& a) {
@@ -153,6 +200,21 @@ hipError_t launch_attn_merge(const MergeArgs& a) {
     else
         hipLaunchKernelGGL((attn_merge_kernel<false, MU>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
                            a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D, rpw);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_pieces(const MergePiecesArgs& a) {
+    const int lpr = (int)(a.D / 4);
+    const int64_t threads = (int64_t)a.n_split * kAttnTileRows * lpr;
+    const int64_t blocks = (threads + 255) / 256;
+    if (a.out_f32)
+        hipLaunchKernelGGL(merge_pieces_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o,
+                           a.ws_lse, a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, a.Sq, (int)a.D,
+                           a.accumulate ? 1 : 0);
+    else
+        hipLaunchKernelGGL(merge_pieces_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o,
+                           a.ws_lse, a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, a.Sq, (int)a.D,
+                           a.accumulate ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -38,8 +38,9 @@ def header_functions():
 
 
 def test_header_declares_expected_entry_points():
-    assert header_functions() == sorted(["cpattn_abi_version", "cpattn_attn_fwd", "cpattn_attn_merge",
-                                         "cpattn_ring_attn_fwd", "cpattn_status_string",
+    assert header_functions() == sorted(["cpattn_abi_version", "cpattn_attn_fwd", "cpattn_attn_fwd_ex",
+                                         "cpattn_attn_fwd_split_plan", "cpattn_attn_fwd_workspace_size",
+                                         "cpattn_attn_merge", "cpattn_ring_attn_fwd", "cpattn_status_string",
                                          "cpattn_ulysses_pack", "cpattn_ulysses_unpack"])
 
 
@@ -54,9 +55,9 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.cpattn_abi_version() == _lib.ABI_VERSION == 1
+    assert L.cpattn_abi_version() == _lib.ABI_VERSION == 2
     seen = set()
-    for s in range(9):
+    for s in range(10):
         msg = L.cpattn_status_string(s)
         assert msg and msg not in seen
         seen.add(msg)
@@ -93,6 +94,94 @@ def test_attn_fwd_validation(L):
     assert fwd(L, lse=C + 1024) == _lib.E_ALIAS
 
 
+W = 0x60000000     # fake workspace
+
+
+def fwd_ex(L, q=A, k=B_, v=C, o=D_, lse=E, B=1, H=2, Sq=256, Skv=256, D=64, scale=0.125, i=0, od=0, flags=0,
+           ws=W, ws_bytes=1 << 20):
+    return L.cpattn_attn_fwd_ex(q, k, v, o, lse, B, H, Sq, Skv, D, scale, i, od, flags, ws, ws_bytes, None)
+
+
+def test_attn_fwd_ex_validation(L):
+    # the attn_fwd checks apply unchanged
+    assert fwd_ex(L, q=None) == _lib.E_NULL
+    assert fwd_ex(L, i=_lib.F32, od=_lib.BF16) == _lib.E_DTYPE
+    assert fwd_ex(L, D=96) == _lib.E_HEADDIM
+    assert fwd_ex(L, scale=0.0) == _lib.E_SCALE
+    assert fwd_ex(L, o=A + 16) == _lib.E_ALIAS
+    # flags
+    assert fwd_ex(L, flags=2) == _lib.E_FLAGS
+    assert fwd_ex(L, flags=0x80000000) == _lib.E_FLAGS
+    # accumulate needs bf16 inputs and an f32 accumulator
+    assert fwd_ex(L, flags=_lib.FLAG_ACCUMULATE, od=_lib.BF16) == _lib.E_DTYPE
+    assert fwd_ex(L, flags=_lib.FLAG_ACCUMULATE, i=_lib.F32, od=_lib.F32) == _lib.E_DTYPE
+    # workspace
+    assert fwd_ex(L, ws=None) == _lib.E_NULL                 # NULL with a size
+    assert fwd_ex(L, ws=W + 8) == _lib.E_ALIGN
+    assert fwd_ex(L, ws=A + 4096) == _lib.E_ALIAS            # on top of q
+    assert fwd_ex(L, ws=D_ - 4096, ws_bytes=8192) == _lib.E_ALIAS   # runs into o
+    assert fwd_ex(L, ws=E, ws_bytes=16) == _lib.E_ALIAS      # on top of lse
+
+
+def plan(L, B=1, H=24, Sq=44160, Skv=44160, D=128, slots=256, ws=2**64 - 1):
+    t, p, b = ctypes.c_int64(-1), ctypes.c_int64(-1), ctypes.c_uint64(1)
+    st = L.cpattn_attn_fwd_split_plan(B, H, Sq, Skv, D, slots, ws, ctypes.byref(t), ctypes.byref(p),
+                                      ctypes.byref(b))
+    assert st == _lib.OK
+    return t.value, p.value, b.value
+
+
+def piece_bytes(D):
+    return 256 * (D + 1) * 4
+
+
+def test_split_plan(L):
+    """The planner's choices, worked out by hand for 256 resident workgroups (one per CU):
+    T tiles of 256 rows leave T mod 256 tiles for the last wave; s pieces of those cost
+    ceil(rem*s/256) * (1/s + 4/nblk) tile-times against 1 for no split."""
+    # video self-attention: 24 * 173 = 4152 tiles, 56 in the last wave, 690 key blocks.
+    # One round: s = 4 (56 * 4 <= 256) costs 0.2558; two rounds of s = 9 (504 pieces)
+    # cost 2 * (1/9 + 4/690) = 0.2338, the minimum
+    assert plan(L) == (56, 9, 56 * 9 * piece_bytes(128))
+    # AllGather-KV rank: 24 * 22 = 528 tiles, 16 left over -> 16 pieces each (0.0683)
+    assert plan(L, Sq=5520) == (16, 16, 256 * piece_bytes(128))
+    # Ulysses rank: 3 * 173 = 519 tiles, 7 left over -> 36 pieces (252 <= 256; 0.0336)
+    assert plan(L, H=3) == (7, 36, 252 * piece_bytes(128))
+    # ring chunk: 528 tiles against 87 key blocks: s <= 21 by the 4-block minimum; 16 (0.108)
+    assert plan(L, Sq=5520, Skv=5520) == (16, 16, 256 * piece_bytes(128))
+    # a full last wave: nothing to split
+    assert plan(L, H=16, Sq=4096) == (0, 1, 0)
+    # 250 of 256 slots busy in the last wave: splitting cannot beat one round
+    assert plan(L, H=22, Sq=5888) == (0, 1, 0)
+    # fewer than 8 key blocks: never split
+    assert plan(L, H=1, Sq=300, Skv=448) == (0, 1, 0)
+    # few tiles, few keys: 8 tiles, 47 blocks -> at most 11 pieces of >= 4 blocks
+    assert plan(L, H=2, Sq=1000, Skv=3000) == (8, 11, 88 * piece_bytes(128))
+    # the workspace bounds the pieces: room for 100 -> 6 per tile of 16
+    assert plan(L, Sq=5520, ws=100 * piece_bytes(128) + 5) == (16, 6, 96 * piece_bytes(128))
+    # room for fewer than two pieces per tile, or no slots known: no split
+    assert plan(L, Sq=5520, ws=31 * piece_bytes(128)) == (0, 1, 0)
+    assert plan(L, slots=0) == (0, 1, 0)
+    # D = 64 pieces are smaller
+    assert plan(L, H=3, D=64) == (7, 36, 252 * piece_bytes(64))
+
+
+def test_split_plan_validation(L):
+    t, p, b = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_uint64()
+    f = L.cpattn_attn_fwd_split_plan
+    assert f(1, 2, 100, 100, 128, 256, 0, None, ctypes.byref(p), ctypes.byref(b)) == _lib.E_NULL
+    assert f(1, 2, 0, 100, 128, 256, 0, ctypes.byref(t), ctypes.byref(p), ctypes.byref(b)) == _lib.E_SHAPE
+    assert f(1, 2, 100, 100, 96, 256, 0, ctypes.byref(t), ctypes.byref(p), ctypes.byref(b)) == _lib.E_HEADDIM
+    assert f(1, 2, 100, 100, 128, -1, 0, ctypes.byref(t), ctypes.byref(p), ctypes.byref(b)) == _lib.E_SHAPE
+    n = ctypes.c_uint64()
+    assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 128, 0, 0, None) == _lib.E_NULL
+    assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 128, 7, 0, ctypes.byref(n)) == _lib.E_DTYPE
+    assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 48, 0, 0, ctypes.byref(n)) == _lib.E_HEADDIM
+    # f32 inputs never split: answered without asking the device
+    assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 128, 1, 1, ctypes.byref(n)) == _lib.OK
+    assert n.value == 0
+
+
 def merge(L, oa=A, la=B_, ob=C, lb=D_, oo=E, lo=0x60000000, B=1, H=2, S=100, D=128, dt=0):
     return L.cpattn_attn_merge(oa, la, ob, lb, oo, lo, B, H, S, D, dt, None)
 
@@ -117,7 +206,8 @@ def ring(L, q=A, k=B_, v=C, o=D_, lse=E, ow=0x60000000, lw=0x70000000, n=8, Skv=
 
 def test_ring_validation(L):
     assert ring(L, q=None) == _lib.E_NULL
-    assert ring(L, ow=None) == _lib.E_NULL
+    assert ring(L, ow=None) == _lib.E_NULL             # one work buffer without the other
+    assert ring(L, lw=None) == _lib.E_NULL
     assert ring(L, n=0) == _lib.E_SHAPE
     assert ring(L, D=80) == _lib.E_HEADDIM
     assert ring(L, scale=0.0) == _lib.E_SCALE
