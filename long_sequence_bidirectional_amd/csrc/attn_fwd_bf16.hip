@@ -25,15 +25,16 @@
 //   supplies slots (h, 0..7) = S^T registers 8*(t%2)..+7 of key tile t/2,
 //   i.e. keys 16t + 8*(j/4) + 4h + j%4.
 //
-// LDS.  Q (256 x D, loaded once), K and V blocks (three buffers each) are stored
-// row-major with 16-byte chunks XOR-swizzled per row and filled by direct
+// Registers and LDS.  Each wave keeps its Q^T operand (32 rows x D) in
+// registers for the whole tile.  K and V blocks (three buffers each) are stored
+// in LDS row-major with 16-byte chunks XOR-swizzled per row and filled by direct
 // global->LDS loads (global_load_lds_dwordx4: lane i writes bytes 16i..16i+15
 // of a 1 KB piece, so a wave's load is a plain copy and needs no registers).
 // The V^T A-operand of the PV product comes from two ds_read_b64_tr_b16 per
 // MFMA: in each 16-lane group, lane L points at row kv0 + L/4, columns
 // d0 + 4(L%4) .. +3 and receives V[kv0 .. kv0+3][d0 + L], i.e. four keys of
 // one head-dim column -- exactly the per-lane k-slots above.  The swizzles
-// make the K/Q reads (16 rows x one chunk) and the V transposing reads
+// make the K reads (16 rows x one chunk) and the V transposing reads
 // (4 rows x 4 chunks) hit 64 distinct banks.
 //
 // Schedule.  Per key block j a wave runs an MFMA slot M_j = {S_j = K_j Q^T,
@@ -41,7 +42,7 @@
 // weights, rescale of O when needed).  Waves w and w+4 share a SIMD; group 1
 // (waves 4-7) runs one slot behind group 0, so on every SIMD one wave issues
 // MFMAs while the other computes exponentials, with one workgroup barrier
-// per slot.  In an MFMA slot the operand reads run six MFMAs ahead.  Global
+// per slot.  In an MFMA slot the operand reads run three MFMAs ahead.  Global
 // loads are issued from softmax slots, two slots before their data is needed
 // (three K/V buffers), and the slot barriers are plain s_barrier: each wave
 // waits only for its own older loads (vmcnt) before arriving.
@@ -69,7 +70,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = kAttnTileRows;    // query rows per workgroup (8 waves x 32)
 constexpr int kBN = 64;               // keys per block
-constexpr int kReadAhead = 6;         // MFMA operand reads issued this many MFMAs ahead
+constexpr int kReadAhead = 3;         // MFMA operand reads issued this many MFMAs ahead
 constexpr int NBUF = 3;               // K and V buffers in LDS
 constexpr float kRescaleTh = 8.0f;    // raise m only when the block max exceeds it by > 2^8
 
@@ -101,14 +102,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     constexpr int BLK_BYTES = BN * D * 2;
     constexpr int LOADS_PER_WAVE = BLK_BYTES / 1024 / 8;
     constexpr int ROWS_PER_LOAD = 1024 / (2 * D);
-    constexpr int Q_LOADS = 32 * D * 2 / 1024;
     constexpr int NQK = NKT * NKS;          // MFMA jobs of S = K Q^T
     constexpr int NPV = NDT * NPB;          // MFMA jobs of O += V^T P^T
     static_assert(LOADS_PER_WAVE >= 1, "block too small for the loader");
 
     __shared__ __attribute__((aligned(1024))) uint16_t Ks[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs[NBUF][BN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t Qs[kBM * D];
 
     // Work unit of this workgroup.  Workgroup ids are dealt round-robin over the
     // XCDs; both parts of the grid are mapped so that each XCD walks a contiguous
@@ -154,15 +153,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* vp = v + ((size_t)bh * Skv_all + (size_t)kb0 * BN) * D;
     const int qrow = qt * kBM + wave * 32 + l32;
 
-    // ---- direct global -> LDS loads (rows clamped to the last valid one)
-    auto load_rows = [&](const uint16_t* src, uint16_t* dst, int row0, int nvalid, int inst,
-                         bool is_v) CPATTN_AI {
-        const int row = inst * ROWS_PER_LOAD + lane / NC;
-        const int ch = (lane % NC) ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
-        const int r = min(row0 + row, nvalid - 1);
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src + (size_t)r * D + ch * 8),
-                                         LDS_PTR(void, dst + inst * 512), 16, 0, 0);
-    };
+    // ---- direct global -> LDS loads of K/V blocks (rows clamped to the last valid one)
     auto load_block = [&](const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
         uint16_t* base = dst + wave * LOADS_PER_WAVE * 512;
         auto one = [&]<int I>(ic<I>) CPATTN_AI {
@@ -177,17 +168,20 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     };
     auto wait_loads = [&]() CPATTN_AI { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-    // Q tile: this wave's 32 rows, swizzled like K.
+    // Q^T operand of this wave, held in registers for the whole tile: for k-step ks lane
+    // (l32, hh) holds q[row l32][16 ks + 8 hh .. +7], read straight from global memory
+    // (rows past Sq clamped to the last valid one).
+    u32x4 qreg[NKS];
+    {
+        const uint16_t* qr = qp + (size_t)min(qrow, Sq - 1) * D + 8 * hh;
 #pragma unroll
-    for (int i = 0; i < Q_LOADS; ++i) load_rows(qp, Qs, qt * kBM, Sq, wave * Q_LOADS + i, false);
+        for (int ks = 0; ks < NKS; ++ks) qreg[ks] = *reinterpret_cast<const u32x4*>(qr + 16 * ks);
+    }
 
     // ---- LDS read addresses: lane-dependent parts (elements); the rest folds into offsets
-    int qoff[NKS], koff[NKS], voff[NDT];
+    int koff[NKS], voff[NDT];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        qoff[ks] = (wave * 32 + l32) * D + (((2 * ks + hh) ^ swz_k<D>(wave * 32 + l32)) * 8);
-        koff[ks] = l32 * D + (((2 * ks + hh) ^ swz_k<D>(l32)) * 8);
-    }
+    for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * D + (((2 * ks + hh) ^ swz_k<D>(l32)) * 8);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
         const int col = dt * 32 + 16 * g16 + 4 * (L16 & 3);
@@ -234,13 +228,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
                 for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
         }
         u32x4 frag[NJ];
-        u32x4 qfr[NKS];
         auto rd = [&]<int I>(ic<I>) CPATTN_AI {
             constexpr int jid = J0 + I;
             if constexpr (jid < NQK) {
                 constexpr int kt = jid % NKT, ks = jid / NKT;
                 frag[I] = read_k(ic<KB>{}, kt, ks);
-                if constexpr (kt == 0) qfr[ks] = *reinterpret_cast<const u32x4*>(&Qs[qoff[ks]]);
             } else {
                 constexpr int p = jid - NQK;
                 frag[I] = read_vt(ic<VB>{}, p % NDT, p / NDT);
@@ -252,7 +244,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
             if constexpr (jid < NQK) {
                 constexpr int kt = jid % NKT, ks = jid / NKT;
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, frag[I]),
-                                                                __builtin_bit_cast(bf16x8, qfr[ks]), s[kt],
+                                                                __builtin_bit_cast(bf16x8, qreg[ks]), s[kt],
                                                                 0, 0, 0);
             } else {
                 constexpr int p = jid - NQK, dt = p % NDT, t = p / NDT;
