@@ -309,6 +309,27 @@ def secondary_rows(cp, torch, q, k, v, stream):
     out["ulysses_rank_tflops"] = round(uly_flops / ms / 1e9, 1)
     ms = timeit(lambda: cp.attn_fwd(q3, k3, v3, o=o3, lse=l3, stream=stream), 5)
     out["ulysses_rank_unsplit_tflops"] = round(uly_flops / ms / 1e9, 1)
+    # the rank's local work between the two all-to-alls, from the receive buffers of Q, K, V
+    # ([P, S_l, Hp, D] each) to the send buffer of O: unpack x3 + head-major attention + pack,
+    # against sequence-major attention reading and writing those buffers in place
+    recv = [x.transpose(1, 2).contiguous() for x in (q3, k3, v3)]          # [1, S, 3, D] = [1, P, S_l, 3, D]
+    o_send = torch.empty_like(recv[0])
+    ws3s = workspace(cp, torch, 1, 3, inputs.S_VIDEO, inputs.S_VIDEO, D)
+    r5 = [x.view(1, P, S_L, H // P, D) for x in recv]
+    unpacked = [torch.empty_like(q3) for _ in range(3)]
+
+    def unfused():
+        for src, dst in zip(r5, unpacked):
+            cp.ulysses_unpack(src, P, cp.SEQ_TO_HEAD, dst=dst, stream=stream)
+        cp.attn_fwd_ex(unpacked[0], unpacked[1], unpacked[2], o=o3, lse=l3, workspace=ws3, stream=stream)
+        cp.ulysses_pack(o3, P, cp.HEAD_TO_SEQ, dst=o_send.view(1, P, S_L, H // P, D), stream=stream)
+
+    ms_unfused = timeit(unfused, 5)
+    ms_fused = timeit(lambda: cp.attn_fwd_ex(recv[0], recv[1], recv[2], o=o_send, lse=l3, workspace=ws3s,
+                                             seq_major=True, stream=stream), 5)
+    out["ulysses_rank_local_unfused_ms"] = round(ms_unfused, 3)
+    out["ulysses_rank_local_fused_ms"] = round(ms_fused, 3)
+    out["ulysses_rank_fused_tflops"] = round(uly_flops / ms_fused / 1e9, 1)
     # merge (f32 O, the ring partial format): reads 2 O + 2 LSE, writes 1 O + 1 LSE
     ms = timeit(lambda: cp.attn_merge(o, l, ow, lw, o_out=o, lse_out=l, stream=stream))
     merge_bytes = 3 * o.numel() * 4 + 3 * l.numel() * 4

@@ -86,6 +86,7 @@ typedef enum {
 
 /* Flags of cpattn_attn_fwd_ex. */
 #define CPATTN_FLAG_ACCUMULATE 1u
+#define CPATTN_FLAG_SEQ_MAJOR 2u
 
 typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
 
@@ -128,7 +129,8 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
  *                    ignored and undefined on return.  Must not overlap any
  *                    tensor argument (CPATTN_E_ALIAS); NULL with a nonzero
  *                    size is CPATTN_E_NULL.
- *   flags            0 or CPATTN_FLAG_ACCUMULATE; other bits -> CPATTN_E_FLAGS.
+ *   flags            any of CPATTN_FLAG_ACCUMULATE, CPATTN_FLAG_SEQ_MAJOR; other
+ *                    bits -> CPATTN_E_FLAGS.
  *
  * Workspace.  The bf16 kernel runs 256 query rows of one (b, h) per
  * workgroup; when the tiles do not fill the device's last wave, the keys of
@@ -146,6 +148,15 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
  * each row is folded with the attn_merge rule in f32.  Requires in_dtype =
  * BF16 and o_dtype = F32 (else CPATTN_E_DTYPE).  With Skv = 0 the call
  * leaves (o, lse) unchanged.
+ *
+ * CPATTN_FLAG_SEQ_MAJOR.  q, k, v and o are sequence-major (token-major):
+ * q [B, Sq, H, D], k and v [B, Skv, H, D], o [B, Sq, H, D]; lse stays
+ * [B, H, Sq].  This is the layout of a rank's token shard and, with
+ * H = H_total / P, of the DeepSpeed Ulysses receive buffer [P, S_local, H, D]
+ * read as [S, H, D] (first page, "DeepSpeed Ulysses"): attention reads that
+ * buffer in place and writes o straight into the send buffer of the second
+ * all-to-all, so no relayout pass is needed on the head side.  Same results
+ * as the head-major call on the transposed tensors, bit for bit.
  */
 cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,

@@ -19,7 +19,8 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import (BF16, F32, FLAG_ACCUMULATE, HEAD_TO_SEQ, SEQ_TO_HEAD, CpattnError, check, lib)
+from ._lib import (BF16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD, CpattnError, check,
+                   lib)
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
            "SEQ_TO_HEAD", "HEAD_TO_SEQ", "CpattnError", "lib"]
@@ -53,22 +54,30 @@ def _stream(stream):
     return s.cuda_stream
 
 
-def _attn_operands(q, k, v, o, lse, scale, out_dtype):
+def _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major=False):
+    """Shapes, defaults and the C argument tuple of an attention call.  Head-major tensors are
+    [B, H, S, D]; sequence-major ones [B, S, H, D]; lse is [B, H, Sq] either way."""
     torch = _torch()
-    B, H, Sq, D = q.shape
-    Skv = k.shape[2]
-    if k.shape != (B, H, Skv, D) or v.shape != k.shape:
+    if seq_major:
+        B, Sq, H, D = q.shape
+        Skv = k.shape[1]
+        kv_shape, o_shape = (B, Skv, H, D), (B, Sq, H, D)
+    else:
+        B, H, Sq, D = q.shape
+        Skv = k.shape[2]
+        kv_shape, o_shape = (B, H, Skv, D), (B, H, Sq, D)
+    if tuple(k.shape) != kv_shape or v.shape != k.shape:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if o is None:
-        o = torch.empty((B, H, Sq, D), dtype=out_dtype or q.dtype, device=q.device)
+        o = torch.empty(o_shape, dtype=out_dtype or q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if o.shape != q.shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
-        raise ValueError("o must be [B,H,Sq,D] and lse float32 [B,H,Sq]")
+    if tuple(o.shape) != o_shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
+        raise ValueError(f"o must be {o_shape} and lse float32 [B,H,Sq]")
     args = (_dev(q, "q"), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None, _dev(o, "o"),
             _dev(lse, "lse"), B, H, Sq, Skv, D, float(scale), _dtype_code(q), _dtype_code(o))
     return o, lse, args
@@ -82,16 +91,17 @@ def attn_fwd(q, k, v, o=None, lse=None, scale=None, out_dtype=None, stream=None)
 
 
 def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, out_dtype=None, workspace=None, accumulate=False,
-                stream=None):
-    """attn_fwd with a workspace (uint8 device tensor, key-range split of the last wave) and an
-    accumulate mode that folds the result into the f32 (o, lse) already there."""
+                seq_major=False, stream=None):
+    """attn_fwd with a workspace (uint8 device tensor, key-range split of the last wave), an
+    accumulate mode that folds the result into the f32 (o, lse) already there, and a
+    sequence-major layout (q [B,Sq,H,D], k/v [B,Skv,H,D], o [B,Sq,H,D])."""
     if accumulate and (o is None or lse is None):
         raise ValueError("accumulate needs the existing o and lse")
-    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype)
+    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None and workspace.numel() > 0:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    flags = FLAG_ACCUMULATE if accumulate else 0
+    flags = (FLAG_ACCUMULATE if accumulate else 0) | (FLAG_SEQ_MAJOR if seq_major else 0)
     check("cpattn_attn_fwd_ex", lib().cpattn_attn_fwd_ex(*args, flags, ws_ptr, ws_bytes, _stream(stream)))
     return o, lse
 

@@ -17,6 +17,7 @@ BF16, F32 = 0, 1
 SEQ_TO_HEAD, HEAD_TO_SEQ = 0, 1
 ABI_VERSION = 2
 FLAG_ACCUMULATE = 1
+FLAG_SEQ_MAJOR = 2
 
 STATUS_NAMES = {OK: "OK", E_NULL: "E_NULL", E_SHAPE: "E_SHAPE", E_DTYPE: "E_DTYPE", E_HEADDIM: "E_HEADDIM",
                 E_ALIGN: "E_ALIGN", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP", E_SCALE: "E_SCALE",

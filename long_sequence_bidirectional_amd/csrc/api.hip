@@ -147,17 +147,44 @@ int64_t device_slots(int64_t D, bool out_f32) {
     return v;
 }
 
+// Strides of an attention operand with S rows per (b, h) in the given layout.
+cpattn::Strides layout_strides(int64_t H, int64_t S, int64_t D, bool seq_major) {
+    if (seq_major) return cpattn::Strides{S * H * D, D, H * D};
+    return cpattn::Strides{H * S * D, S * D, D};
+}
+
 // Attention of one K/V set into (o, lse): written, or folded into them when accumulate.
 // ws_o/ws_lse (capacity ws_pieces pieces each) hold the partials of a split; null = no split.
-cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t Sq,
-                       int64_t Skv, int64_t D, float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
-                       bool accumulate, float* ws_o, float* ws_lse, int64_t ws_pieces, hipStream_t stream) {
+cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                       int64_t Sq, int64_t Skv, int64_t D, float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
+                       bool accumulate, bool seq_major, float* ws_o, float* ws_lse, int64_t ws_pieces,
+                       hipStream_t stream) {
+    const int64_t BH = B * H;
     if (Skv == 0) {   // empty key set: O = 0, LSE = -inf, the identity of the fold
         if (accumulate) return CPATTN_OK;
         return hip_status(cpattn::launch_fill_empty(o, BH * Sq * D * dtype_size(o_dtype), lse, BH * Sq, stream));
     }
-    cpattn::AttnFwdArgs a{q, k, v, o, lse, BH, Sq, Skv, D, scale, o_dtype == CPATTN_F32, accumulate,
-                          0, 1, nullptr, nullptr, stream};
+    cpattn::AttnFwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.BH = BH;
+    a.H = H;
+    a.seq_major = seq_major;
+    a.sq = layout_strides(H, Sq, D, seq_major);
+    a.skv = layout_strides(H, Skv, D, seq_major);
+    a.so = a.sq;
+    a.Sq = Sq;
+    a.Skv = Skv;
+    a.D = D;
+    a.scale = scale;
+    a.out_f32 = o_dtype == CPATTN_F32;
+    a.accumulate = accumulate;
+    a.split_tiles = 0;
+    a.split_pieces = 1;
+    a.stream = stream;
     if (in_dtype != CPATTN_BF16) return hip_status(cpattn::launch_attn_fwd_f32(a));
     if (ws_o && ws_lse && ws_pieces > 0) {
         const SplitPlan p = plan_split(BH, Sq, Skv, D, device_slots(D, a.out_f32),
@@ -210,7 +237,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd(const void* q, const void* k, const 
     AttnFwdCheck ck;
     const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, &ck);
     if (st != CPATTN_OK) return st;
-    return run_attn(q, k, v, o, lse, B * H, Sq, Skv, D, scale, in_dtype, o_dtype, false, nullptr, nullptr, 0,
+    return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, false, false, nullptr, nullptr, 0,
                     stream);
 }
 
@@ -219,8 +246,9 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, con
                                                float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
                                                uint32_t flags, void* workspace, uint64_t workspace_bytes,
                                                hipStream_t stream) {
-    if ((flags & ~(uint32_t)CPATTN_FLAG_ACCUMULATE) != 0) return CPATTN_E_FLAGS;
+    if ((flags & ~(uint32_t)(CPATTN_FLAG_ACCUMULATE | CPATTN_FLAG_SEQ_MAJOR)) != 0) return CPATTN_E_FLAGS;
     const bool acc = (flags & CPATTN_FLAG_ACCUMULATE) != 0;
+    const bool seq_major = (flags & CPATTN_FLAG_SEQ_MAJOR) != 0;
     AttnFwdCheck ck;
     const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, &ck);
     if (st != CPATTN_OK) return st;
@@ -240,8 +268,8 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, con
         ws_o = static_cast<float*>(workspace);
         ws_lse = ws_o + (size_t)ws_pieces * cpattn::kAttnTileRows * D;
     }
-    return run_attn(q, k, v, o, lse, B * H, Sq, Skv, D, scale, in_dtype, o_dtype, acc, ws_o, ws_lse, ws_pieces,
-                    stream);
+    return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, acc, seq_major, ws_o, ws_lse,
+                    ws_pieces, stream);
 }
 
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd_split_plan(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
@@ -329,7 +357,6 @@ CPATTN_EXPORT cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_ch
         for (int j = i + 1; j < 4; ++j)
             if (overlap(outs[i], outs[j])) return CPATTN_E_ALIAS;
     }
-    const int64_t BH = B * H;
     const int64_t chunk_bytes = c.kv_elems * 2;
     // o_work / lse_work hold the key-range pieces of split tiles (one tile of rows each)
     const int64_t ws_pieces = (o_work && lse_work) ? c.rows / cpattn::kAttnTileRows : 0;
@@ -337,8 +364,8 @@ CPATTN_EXPORT cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_ch
     for (int64_t ch = 0; ch < n_chunks && s == CPATTN_OK; ++ch) {
         const char* kc = static_cast<const char*>(k_chunks) + ch * chunk_bytes;
         const char* vc = static_cast<const char*>(v_chunks) + ch * chunk_bytes;
-        s = run_attn(q, kc, vc, o, lse, BH, Sq, Skv_chunk, D, scale, CPATTN_BF16, CPATTN_F32, ch > 0, o_work,
-                     lse_work, ws_pieces, stream);
+        s = run_attn(q, kc, vc, o, lse, B, H, Sq, Skv_chunk, D, scale, CPATTN_BF16, CPATTN_F32, ch > 0, false,
+                     o_work, lse_work, ws_pieces, stream);
     }
     return s;
 }

@@ -89,10 +89,11 @@ __device__ __forceinline__ int swz_v(int r) {     // V: 4 consecutive rows x 4 c
     return 4 * ((r / RPB) % (D / 32));
 }
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool SEQ>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, AttnTileMap map, float c) {
+    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
+    Strides so, AttnTileMap map, float c) {
     constexpr int BN = kBN;
     constexpr int NC = D / 8;               // 16-byte chunks per row
     constexpr int NKS = D / 16;             // k-steps of the QK^T product
@@ -148,9 +149,15 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     const int g16 = (lane >> 4) & 1;
     const int group = wave >> 2;            // waves w and w+4 share a SIMD
 
-    const uint16_t* qp = q + (size_t)bh * Sq * D;
-    const uint16_t* kp = k + ((size_t)bh * Skv_all + (size_t)kb0 * BN) * D;
-    const uint16_t* vp = v + ((size_t)bh * Skv_all + (size_t)kb0 * BN) * D;
+    // Row strides: D for head-major operands (compile time), runtime for sequence-major ones.
+    const int64_t q_row = SEQ ? sq.row : D, kv_row = SEQ ? skv.row : D, o_row = SEQ ? so.row : D;
+    const int b = SEQ ? bh / H : 0, h = SEQ ? bh - b * H : 0;
+    const int64_t q_base = SEQ ? b * sq.batch + h * sq.head : (int64_t)bh * Sq * D;
+    const int64_t o_base = SEQ ? b * so.batch + h * so.head : (int64_t)bh * Sq * D;
+    const int64_t kv_off = (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv_all * D) + (int64_t)kb0 * BN * kv_row;
+    const uint16_t* qp = q + q_base;
+    const uint16_t* kp = k + kv_off;
+    const uint16_t* vp = v + kv_off;
     const int qrow = qt * kBM + wave * 32 + l32;
 
     // ---- direct global -> LDS loads of K/V blocks (rows clamped to the last valid one)
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
             const int row = (wave * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
             const int ch = (lane % NC) ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
             const int r = min(j * BN + row, Skv - 1);
-            const char* g = reinterpret_cast<const char*>(src + (size_t)r * D + ch * 8) - I * 1024;
+            const char* g = reinterpret_cast<const char*>(src + r * kv_row + ch * 8) - I * 1024;
             __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, g), LDS_PTR(void, base), 16, I * 1024, 0);
         };
         [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI { (one(ic<Is>{}), ...); }(
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     // (rows past Sq clamped to the last valid one).
     u32x4 qreg[NKS];
     {
-        const uint16_t* qr = qp + (size_t)min(qrow, Sq - 1) * D + 8 * hh;
+        const uint16_t* qr = qp + min(qrow, Sq - 1) * q_row + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qreg[ks] = *reinterpret_cast<const u32x4*>(qr + 16 * ks);
     }
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
             }
         if (hh == 0) map.ws_lse[wrow] = lse_new;
     } else if (qrow < Sq) {
-        const size_t orow = ((size_t)bh * Sq + qrow) * D;
+        const int64_t orow = o_base + qrow * o_row;
         float wa = 0.f, wb = inv, L = lse_new;   // O = wa * O_old + wb * acc
         if (OUT_F32 && map.accumulate) {
             const float la = lse[(size_t)bh * Sq + qrow];
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_kernel(
     }
 }
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool SEQ>
 hipError_t launch(const AttnFwdArgs& a) {
     const int nQt = (int)((a.Sq + kBM - 1) / kBM);
     const int64_t total = (int64_t)a.BH * nQt;
@@ -442,29 +449,36 @@ hipError_t launch(const AttnFwdArgs& a) {
     m.accumulate = a.accumulate ? 1 : 0;
     const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;
     const float c = (float)((double)a.scale * 1.4426950408889634);
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32>), dim3(grid), dim3(512), 0, a.stream,
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OUT_F32, SEQ>), dim3(grid), dim3(512), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                       static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, m, c);
+                       static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)a.H, a.sq,
+                       a.skv, a.so, m, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_tiles == 0) return e;
-    MergePiecesArgs f{a.ws_o, a.ws_lse, a.o, a.lse, m.n_dp, m.n_split, m.split_s, nQt, a.Sq, a.D, a.out_f32,
-                      a.accumulate, a.stream};
+    MergePiecesArgs f{a.ws_o, a.ws_lse, a.o, a.lse, m.n_dp, m.n_split, m.split_s, nQt, a.H, a.so, a.Sq, a.D,
+                      a.out_f32, a.accumulate, a.stream};
     return launch_merge_pieces(f);
 }
 
 template <int D, bool OUT_F32>
 int occupancy() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<D, OUT_F32>, 512, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_bf16_kernel<D, OUT_F32, false>, 512, 0) !=
+        hipSuccess)
         return 0;
     return n;
 }
 
 }  // namespace
 
+template <int D, bool OUT_F32>
+hipError_t launch_layout(const AttnFwdArgs& a) {
+    return a.seq_major ? launch<D, OUT_F32, true>(a) : launch<D, OUT_F32, false>(a);
+}
+
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a) {
-    if (a.D == 128) return a.out_f32 ? launch<128, true>(a) : launch<128, false>(a);
-    return a.out_f32 ? launch<64, true>(a) : launch<64, false>(a);
+    if (a.D == 128) return a.out_f32 ? launch_layout<128, true>(a) : launch_layout<128, false>(a);
+    return a.out_f32 ? launch_layout<64, true>(a) : launch_layout<64, false>(a);
 }
 
 int attn_fwd_bf16_blocks_per_cu(int64_t D, bool out_f32) {

@@ -30,7 +30,7 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                            const float* __restrict__ v, float* __restrict__ o,
                                                            float* __restrict__ lse, int Sq, int Skv, int nQt,
-                                                           float c) {
+                                                           int H, Strides sq, Strides skv, Strides so, float c) {
     constexpr int NI = D / 32;   // float4 groups per lane
     __shared__ __attribute__((aligned(16))) float Kf[FBN * D];
     __shared__ __attribute__((aligned(16))) float Vf[FBN * D];
@@ -41,14 +41,15 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float* __restri
     const int r = tid >> 3;
     const int sub = tid & 7;
     const int qrow = qt * FBM + r;
-    const float* qp = q + (size_t)bh * Sq * D;
-    const float* kp = k + (size_t)bh * Skv * D;
-    const float* vp = v + (size_t)bh * Skv * D;
+    const int b = bh / H, h = bh - (bh / H) * H;
+    const float* qp = q + b * sq.batch + h * sq.head;
+    const float* kp = k + b * skv.batch + h * skv.head;
+    const float* vp = v + b * skv.batch + h * skv.head;
 
     f32x4 qv[NI], ov[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        qv[i] = qrow < Sq ? *reinterpret_cast<const f32x4*>(qp + (size_t)qrow * D + sub * 4 + 32 * i)
+        qv[i] = qrow < Sq ? *reinterpret_cast<const f32x4*>(qp + qrow * sq.row + sub * 4 + 32 * i)
                           : f32x4{0.f, 0.f, 0.f, 0.f};
         ov[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float* __restri
             const int key = j * FBN + row;
             f32x4 kv4 = {0.f, 0.f, 0.f, 0.f}, vv4 = {0.f, 0.f, 0.f, 0.f};
             if (key < Skv) {
-                kv4 = reinterpret_cast<const f32x4*>(kp + (size_t)key * D)[col];
-                vv4 = reinterpret_cast<const f32x4*>(vp + (size_t)key * D)[col];
+                kv4 = reinterpret_cast<const f32x4*>(kp + key * skv.row)[col];
+                vv4 = reinterpret_cast<const f32x4*>(vp + key * skv.row)[col];
             }
             reinterpret_cast<f32x4*>(Kf)[e] = kv4;
             reinterpret_cast<f32x4*>(Vf)[e] = vv4;
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float* __restri
 
     if (qrow < Sq) {
         const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-        float* orow = o + ((size_t)bh * Sq + qrow) * D;
+        float* orow = o + b * so.batch + h * so.head + qrow * so.row;
 #pragma unroll
         for (int i = 0; i < NI; ++i) *reinterpret_cast<f32x4*>(orow + sub * 4 + 32 * i) = ov[i] * inv;
         if (sub == 0) lse[(size_t)bh * Sq + qrow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
@@ -130,12 +131,12 @@ hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a) {
         hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, dim3((unsigned)grid), dim3(256), 0, a.stream,
                            static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                            static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, (int)a.Sq,
-                           (int)a.Skv, nQt, c);
+                           (int)a.Skv, nQt, (int)a.H, a.sq, a.skv, a.so, c);
     else
         hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, dim3((unsigned)grid), dim3(256), 0, a.stream,
                            static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                            static_cast<const float*>(a.v), static_cast<float*>(a.o), a.lse, (int)a.Sq,
-                           (int)a.Skv, nQt, c);
+                           (int)a.Skv, nQt, (int)a.H, a.sq, a.skv, a.so, c);
     return hipGetLastError();
 }
 

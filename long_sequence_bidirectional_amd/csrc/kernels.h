@@ -10,6 +10,13 @@ namespace cpattn {
 // Query rows per workgroup tile of the bf16 attention kernel.
 constexpr int kAttnTileRows = 256;
 
+// Element strides of an attention operand: element (b, h, s, d) sits at
+// b * batch + h * head + s * row + d.  Head-major [B,H,S,D]: row = D,
+// head = S*D; sequence-major [B,S,H,D]: row = H*D, head = D.
+struct Strides {
+    int64_t batch, head, row;
+};
+
 struct AttnFwdArgs {
     const void* q;
     const void* k;
@@ -17,6 +24,9 @@ struct AttnFwdArgs {
     void* o;
     float* lse;
     int64_t BH;      // B * H
+    int64_t H;
+    bool seq_major;        // operands [B,S,H,D] (else [B,H,S,D]); the strides below agree
+    Strides sq, skv, so;   // of q, of k and v, of o (lse is always [B, H, Sq])
     int64_t Sq;
     int64_t Skv;     // >= 1 (Skv == 0 is handled by launch_fill_empty)
     int64_t D;       // 64 or 128
@@ -60,6 +70,8 @@ struct MergePiecesArgs {
     int n_split;
     int pieces;
     int nQt;          // tiles per (b, h)
+    int64_t H;
+    Strides so;       // of o
     int64_t Sq;
     int64_t D;
     bool out_f32;

@@ -136,8 +136,8 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const void* o_a, c
 template <bool F32>
 __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restrict__ ws_o,
                                                            const float* __restrict__ ws_lse, void* o, float* lse,
-                                                           int first_tile, int n_split, int pieces, int nQt,
-                                                           int64_t Sq, int D, int accumulate) {
+                                                           int first_tile, int n_split, int pieces, int nQt, int H,
+                                                           Strides so, int64_t Sq, int D, int accumulate) {
     constexpr int TR = kAttnTileRows;
     const int lpr = D >> 2;                       // lanes per row
     const int64_t grow = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / lpr;
@@ -149,7 +149,8 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restri
     const int bh = tile / nQt;
     const int64_t qrow = (int64_t)(tile - bh * nQt) * TR + r;
     if (qrow >= Sq) return;
-    const size_t row = (size_t)bh * Sq + qrow;
+    const size_t row = (size_t)bh * Sq + qrow;                                  // lse index
+    const int64_t orow = (bh / H) * so.batch + (bh % H) * so.head + qrow * so.row;   // o offset
     const float* lp = ws_lse + (size_t)ti * pieces * TR + r;
     const float* op = ws_o + ((size_t)ti * pieces * TR + r) * D + c4;
     const float la = accumulate ? lse[row] : -INFINITY;
@@ -161,15 +162,15 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restri
         float tot = expf(la - mx);
         for (int p = 0; p < pieces; ++p) tot += expf(lp[(size_t)p * TR] - mx);
         L = mx + logf(tot);
-        if (accumulate) acc = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + row * D + c4) *
+        if (accumulate) acc = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow + c4) *
                               expf(la - L);
         for (int p = 0; p < pieces; ++p)
             acc += *reinterpret_cast<const f32x4*>(op + (size_t)p * TR * D) * expf(lp[(size_t)p * TR] - L);
     }
     if constexpr (F32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + row * D + c4) = acc;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + c4) = acc;
     } else {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + row * D + c4) =
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + c4) =
             u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
     }
     if (c4 == 0) lse[row] = L;
@@ -209,12 +210,12 @@ hipError_t launch_merge_pieces(const MergePiecesArgs& a) {
     const int64_t blocks = (threads + 255) / 256;
     if (a.out_f32)
         hipLaunchKernelGGL(merge_pieces_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o,
-                           a.ws_lse, a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, a.Sq, (int)a.D,
-                           a.accumulate ? 1 : 0);
+                           a.ws_lse, a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, (int)a.H, a.so, a.Sq,
+                           (int)a.D, a.accumulate ? 1 : 0);
     else
         hipLaunchKernelGGL(merge_pieces_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o,
-                           a.ws_lse, a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, a.Sq, (int)a.D,
-                           a.accumulate ? 1 : 0);
+                           a.ws_lse, a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, (int)a.H, a.so, a.Sq,
+                           (int)a.D, a.accumulate ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -110,8 +110,13 @@ def test_attn_fwd_ex_validation(L):
     assert fwd_ex(L, scale=0.0) == _lib.E_SCALE
     assert fwd_ex(L, o=A + 16) == _lib.E_ALIAS
     # flags
-    assert fwd_ex(L, flags=2) == _lib.E_FLAGS
+    assert fwd_ex(L, flags=4) == _lib.E_FLAGS
+    assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR | 8) == _lib.E_FLAGS
     assert fwd_ex(L, flags=0x80000000) == _lib.E_FLAGS
+    # the layout flag keeps every other check
+    assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR, q=None) == _lib.E_NULL
+    assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR, o=A + 16) == _lib.E_ALIAS
+    assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR | _lib.FLAG_ACCUMULATE, od=_lib.BF16) == _lib.E_DTYPE
     # accumulate needs bf16 inputs and an f32 accumulator
     assert fwd_ex(L, flags=_lib.FLAG_ACCUMULATE, od=_lib.BF16) == _lib.E_DTYPE
     assert fwd_ex(L, flags=_lib.FLAG_ACCUMULATE, i=_lib.F32, od=_lib.F32) == _lib.E_DTYPE

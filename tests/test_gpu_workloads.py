@@ -154,3 +154,30 @@ def test_ring_rank(g, dev, agkv_out):
     dl = torch.max(torch.abs(l - l_ag)).item()
     log(f"  ring vs allgather-kv: O max-abs {d.max().item():.3e} mean-abs {d.mean().item():.3e}; LSE {dl:.3e}")
     assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3 and dl <= 1e-3
+
+
+def test_ulysses_fused_all_ranks(g, dev, self_out):
+    """All 8 ranks of the Ulysses path at full size, attention reading the receive buffers in
+    place: pack -> all-to-all -> sequence-major attention (split as planned) -> all-to-all ->
+    unpack gives the 24-head self-attention output."""
+    from test_gpu_layout import ulysses_fused
+    log("case: ulysses fused, 8 ranks, shards [5520,24,128]")
+    tok = {n: dev[n][0].transpose(0, 1).contiguous().unsqueeze(0) for n in ("q", "k", "v")}   # [1, S, 24, D]
+    sh = lambda t: [t[:, r * S_L:(r + 1) * S_L].contiguous() for r in range(P)]
+    o_shards = ulysses_fused(sh(tok["q"]), sh(tok["k"]), sh(tok["v"]), P, use_ws=True)
+    torch.cuda.synchronize()
+    o = torch.cat(o_shards, dim=1)[0].transpose(0, 1).unsqueeze(0)          # [1, 24, S, D]
+    so, _ = self_out
+    d = torch.abs(o.float() - so.float())
+    log(f"  fused Ulysses vs 24-head self-attention: O max-abs {d.max().item():.3e} "
+        f"mean-abs {d.mean().item():.3e}; bit-identical fraction {(d == 0).float().mean().item():.4f}")
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+    # whole tiles run the same arithmetic in both: rows 0..5519 of every head are tiles 0..21,
+    # never split in either plan
+    assert torch.equal(o[:, :, :S_L].contiguous().view(torch.int16), so[:, :, :S_L].contiguous().view(torch.int16))
+    rows = inputs.sample_rows(S, n_random=16)
+    O, L = oracle_rows(g, "q", "k", "v", rows, range(0, H, 5))
+    got = o[:, 0:H:5][:, :, rows]
+    err = np.abs(host64(got) - O)
+    log(f"  sampled rows vs oracle: O max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
