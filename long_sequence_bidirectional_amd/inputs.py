@@ -25,9 +25,16 @@ import numpy as np
 
 SEED = 42
 
-# Stream indices of SeedSequence(SEED).spawn(N_STREAMS).
+# Stream indices of SeedSequence(SEED).spawn(N_STREAMS) (child i depends only on i).
 _STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_KT, _STREAM_VT, _STREAM_SMALL = range(6)
-N_STREAMS = 6
+_STREAM_P4_Q, _STREAM_P4_K, _STREAM_P4_V, _STREAM_P4_W = range(6, 10)
+N_STREAMS = 10
+
+# Shapes of the attention sample of "TensorRT multi-device attention inference in practice"
+# (its single-device run: sequence length 56320, batch 1; 32 heads of 128, fp16; two ranks).
+P4_SEQ = 56320
+P4_HEADS = 32
+P4_RANKS = 2
 
 # Global shapes of the video workload (see module docstring).
 S_VIDEO = 44160
@@ -102,6 +109,33 @@ def small_f32_set(B=1, H=2, S=256, D=64, seed: int = SEED):
     return q, k, v
 
 
+def normal_f16(shape, rng: np.random.Generator, scale: float = 1.0) -> np.ndarray:
+    """N(0, scale^2) draws stored as IEEE fp16 (float32 draws rounded to nearest even)."""
+    return normal_f32(shape, rng, scale).astype(np.float16)
+
+
+def random_f16(shape, seed: int, scale: float = 1.0) -> np.ndarray:
+    return normal_f16(shape, np.random.Generator(np.random.PCG64(seed)), scale)
+
+
+@functools.lru_cache(maxsize=1)
+def p4_set(seed: int = SEED, S: int = P4_SEQ, H: int = P4_HEADS, D: int = HEAD_DIM):
+    """Inputs of the attention sample's single-device run: fp16 q, k, v in its
+    (seq, batch, heads, head_dim) order with batch 1, i.e. [1, S, H, D], and the two
+    RMSNorm weights w_q, w_k [D] (fp16).  All i.i.d. N(0, 1); read-only arrays."""
+    rw = _rng(_STREAM_P4_W, seed)
+    out = {
+        "q": normal_f16((1, S, H, D), _rng(_STREAM_P4_Q, seed)),
+        "k": normal_f16((1, S, H, D), _rng(_STREAM_P4_K, seed)),
+        "v": normal_f16((1, S, H, D), _rng(_STREAM_P4_V, seed)),
+        "w_q": normal_f16((D,), rw),
+        "w_k": normal_f16((D,), rw),
+    }
+    for a in out.values():
+        a.setflags(write=False)
+    return out
+
+
 def random_bf16(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     """Independent seeded bf16 tensor for ad-hoc test shapes."""
     return normal_bf16(shape, np.random.Generator(np.random.PCG64(seed)), scale)
@@ -128,6 +162,8 @@ WORKLOADS = {
                           "per-chunk partials merged by LSE"),
     "video_layer": Workload("video_layer", "bf16 self-attention S=44160 H=24 D=128 plus cross-attention "
                             "to 2992 text tokens, 36 times (one denoising step's layers)"),
+    "p4_sample": Workload("p4_sample", "fp16 QK-RMSNorm prologue + attention, sequence-major [1,56320,32,128]: "
+                          "the single-device run, and one rank of two under AllGather-KV (28160 query rows)"),
 }
 
 

@@ -21,15 +21,23 @@ source pages:
 * ``ulysses_pack`` / ``ulysses_unpack`` / ``alltoall`` -- the
   sequence<->head relayout around DeepSpeed Ulysses' two all-to-alls (same
   page, section "DeepSpeed Ulysses").
+* ``rms_norm`` / ``qk_prologue`` / ``round_to_f16`` / ``round_to_bf16`` -- the
+  QK-RMSNorm prologue of the attention sample (fp32 RMSNorm over head_dim,
+  eps 1e-6, weight, cast to fp16, split score scale), with 16-bit rounding at
+  the casts the page names ("TensorRT multi-device attention inference in
+  practice", step 1).
 
 Pins: see tests/test_oracle.py (brute force, closed forms, invariants,
-library special cases, merge algebra, relayout bijections).
+library special cases, merge algebra, relayout bijections, RMSNorm closed
+forms and torch's rms_norm, 16-bit rounding ties).
 """
 from .attention import attention, attention_rows, lse_natural
 from .merge import merge
 from .relayout import ulysses_pack, ulysses_unpack, alltoall, SEQ_TO_HEAD, HEAD_TO_SEQ
+from .qk_norm import rms_norm, qk_prologue, round_to_f16, round_to_bf16
 
 __all__ = [
     "attention", "attention_rows", "lse_natural", "merge",
     "ulysses_pack", "ulysses_unpack", "alltoall", "SEQ_TO_HEAD", "HEAD_TO_SEQ",
+    "rms_norm", "qk_prologue", "round_to_f16", "round_to_bf16",
 ]

@@ -381,3 +381,139 @@ def test_inputs_are_seeded():
         np.testing.assert_array_equal(x, y)
     assert a[0].shape == (1, 2, 256, 64) and a[0].dtype == np.float32
     assert abs(float(a[0].std()) - 1.0) < 0.05
+
+
+# ------------------------------------------------------------------ QK-RMSNorm prologue
+def pin_rmsnorm_torch(f):
+    """torch's own rms_norm (float64, CPU) on random rows, with a random weight."""
+    x = np.random.Generator(np.random.PCG64(901)).standard_normal((35, 128))
+    w = np.random.Generator(np.random.PCG64(902)).standard_normal(128)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(w), eps=1e-6).numpy()
+    np.testing.assert_allclose(f(x, w, 1e-6), ref, rtol=1e-13, atol=1e-15)
+
+
+def pin_rmsnorm_closed_forms(f):
+    # constant row c: mean(x^2) = c^2, y = c / sqrt(c^2 + eps) * w
+    for c in (3.0, -0.5, 1e-4):
+        x = np.full((1, 16), c)
+        w = np.linspace(-2.0, 2.0, 16)
+        np.testing.assert_allclose(f(x, w, 1e-6), c / math.sqrt(c * c + 1e-6) * w[None], rtol=1e-14, atol=0)
+    # hand example: x = (3, 4), mean of squares 12.5, w = (1, 2)
+    y = f(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 1e-6)
+    r = math.sqrt(12.5 + 1e-6)
+    np.testing.assert_allclose(y, [[3.0 / r, 8.0 / r]], rtol=1e-15)
+    # with w = 1 the output's mean square is mean(x^2) / (mean(x^2) + eps)
+    x = np.random.Generator(np.random.PCG64(903)).standard_normal((8, 64)) * 0.01
+    y = f(x, np.ones(64), 1e-6)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), ms / (ms + 1e-6), rtol=1e-13)
+
+
+def pin_rmsnorm_invariants(f):
+    g = np.random.Generator(np.random.PCG64(904))
+    x, w = g.standard_normal((6, 128)), g.standard_normal(128)
+    # scale invariance up to eps (a > 0); sign flips the output
+    np.testing.assert_allclose(f(10.0 * x, w, 0.0), f(x, w, 0.0), rtol=1e-13)
+    np.testing.assert_allclose(f(-x, w, 1e-6), -f(x, w, 1e-6), rtol=0, atol=0)
+    # rows are independent; the weight acts per element
+    np.testing.assert_allclose(f(x[2:3], w, 1e-6), f(x, w, 1e-6)[2:3], rtol=0, atol=0)
+    np.testing.assert_allclose(f(x, 3.0 * w, 1e-6), 3.0 * f(x, w, 1e-6), rtol=1e-15)
+
+
+RMS_PINS = [pin_rmsnorm_torch, pin_rmsnorm_closed_forms, pin_rmsnorm_invariants]
+
+
+@pytest.mark.parametrize("pin", RMS_PINS, ids=lambda p: p.__name__)
+def test_oracle_rmsnorm_pins(pin):
+    pin(oracle.rms_norm)
+
+
+def _rms_mutant(kind):
+    def f(x, w, eps):
+        x = np.asarray(x, np.float64)
+        w = np.asarray(w, np.float64)
+        if kind == "no_eps":
+            return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) * w
+        if kind == "sum_not_mean":
+            return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * w
+        if kind == "no_weight":
+            return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+        if kind == "rms_times":
+            return x * np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+        if kind == "mean_abs":
+            return x / (np.mean(np.abs(x), axis=-1, keepdims=True) + eps) * w
+        raise ValueError(kind)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["no_eps", "sum_not_mean", "no_weight", "rms_times", "mean_abs"])
+def test_rmsnorm_pins_catch_planted_mistakes(kind):
+    f = _rms_mutant(kind)
+    failed = 0
+    for pin in RMS_PINS:
+        try:
+            pin(f)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"mutant {kind} passed every pin"
+
+
+def test_16bit_rounding_ties_and_library():
+    # fp16: ulp at 1 is 2^-10; 1 + 2^-11 is a tie -> 1 (even), 1 + 3*2^-11 -> 1 + 2^-9 (even)
+    x = np.array([1.0, 1 + 2 ** -11, 1 + 3 * 2 ** -11, 1 + 2 ** -11 + 2 ** -30, -2.0 - 2 ** -10, 65504.0])
+    np.testing.assert_array_equal(oracle.round_to_f16(x).astype(np.float64),
+                                  [1.0, 1.0, 1 + 2 ** -9, 1 + 2 ** -10, -2.0, 65504.0])
+    # bf16: ulp at 1 is 2^-7; ties to even, and just above a tie rounds up
+    y = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -40, -(1 + 2 ** -8), 0.0, 3.0])
+    np.testing.assert_array_equal(oracle.round_to_bf16(y), [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0, 0.0, 3.0])
+    # against torch's conversions on float32 values (torch converts float64 through float32,
+    # which can double-round; on float32 inputs both are a single rounding)
+    z = (np.random.Generator(np.random.PCG64(905)).standard_normal(20000) * 3.0).astype(np.float32)
+    z64 = z.astype(np.float64)
+    np.testing.assert_array_equal(oracle.round_to_f16(z64), torch.from_numpy(z).to(torch.float16).numpy())
+    tb = torch.from_numpy(z).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_to_bf16(z64), tb)
+    # on float64 inputs: the nearest representable value by exact rational distance, ties to even
+    from fractions import Fraction
+    w = np.random.Generator(np.random.PCG64(907)).standard_normal(300) * 3.0
+    for x in w:
+        for got, bits in ((float(oracle.round_to_f16(x)), 11), (float(oracle.round_to_bf16(x)), 8)):
+            m, e = math.frexp(x)
+            step = Fraction(2) ** (e - bits)                 # spacing of the type in x's binade
+            lo = (Fraction(x) / step).__floor__() * step
+            hi = lo + step
+            d_lo, d_hi = Fraction(x) - lo, hi - Fraction(x)
+            want = lo if d_lo < d_hi else hi if d_hi < d_lo else (lo if (lo / step) % 2 == 0 else hi)
+            assert Fraction(got) == want, (x, got, float(want))
+
+
+def test_qk_prologue_steps():
+    g = np.random.Generator(np.random.PCG64(906))
+    x = g.standard_normal((4, 128)).astype(np.float16)
+    w = g.standard_normal(128).astype(np.float16)
+    s = 128 ** -0.25
+    y = oracle.qk_prologue(x, w, 1e-6, s)
+    # every output is a 16-bit value
+    assert np.array_equal(y, y.astype(np.float16).astype(np.float64))
+    # the two roundings: fp16 RMSNorm output, then the fp16 product with the fp16 constant
+    n16 = oracle.round_to_f16(oracle.rms_norm(x.astype(np.float64), w.astype(np.float64), 1e-6))
+    s16 = float(np.float16(s))
+    assert s16 == 0.29736328125                  # 128^-1/4 = 0.297302... rounded to fp16
+    np.testing.assert_array_equal(y, oracle.round_to_f16(n16.astype(np.float64) * s16).astype(np.float64))
+    # without the scale it is the rounded RMSNorm; rounding error at most half an fp16 ulp
+    y0 = oracle.qk_prologue(x, w, 1e-6)
+    exact = oracle.rms_norm(x.astype(np.float64), w.astype(np.float64), 1e-6)
+    ulp = np.spacing(np.abs(exact).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(y0 - exact) <= 0.5 * ulp + 1e-300)
+    # the scale split over Q and K recovers the 1/sqrt(D) score scale to fp16 accuracy
+    assert abs(s16 * s16 - 128 ** -0.5) < 2e-4
+
+
+def test_p4_inputs_recipe():
+    a = inputs.random_f16((3, 5), 11)
+    assert a.dtype == np.float16
+    np.testing.assert_array_equal(a, inputs.random_f32((3, 5), 11).astype(np.float16))
+    # adding streams did not move the existing ones
+    np.testing.assert_array_equal(inputs._rng(0).standard_normal(4),
+                                  np.random.Generator(np.random.PCG64(np.random.SeedSequence(42).spawn(6)[0]))
+                                  .standard_normal(4))
