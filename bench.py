@@ -347,6 +347,61 @@ def secondary_rows(cp, torch, q, k, v, stream):
     out["unpack_s2h_us"] = round(ms * 1e3, 2)
     out["unpack_s2h_GBps"] = round(nbytes / ms / 1e6, 1)
     out.update(cold_rows(cp, torch, stream))
+    out.update(p4_rows(cp, torch, stream))
+    return out
+
+
+def p4_rows(cp, torch, stream, iters=50):
+    """The attention sample of "TensorRT multi-device attention inference in practice":
+    fp16 (seq, batch=1, 32, 128) tensors, QK-RMSNorm prologue (eps 1e-6, weights, cast to
+    fp16, (1/128)^(1/4) on each of Q and K), then attention; timed as the sample times it,
+    1 warm-up and 50 iterations.  Single-device run: S = 56320; one rank of two under
+    AllGather-KV: its 28160 query rows against the gathered 56320 keys (the K prologue runs
+    on the gathered keys, the Q prologue on the local rows)."""
+    import numpy as np
+    from long_sequence_bidirectional_amd import inputs
+    S, H, D = inputs.P4_SEQ, inputs.P4_HEADS, inputs.HEAD_DIM
+    S_r = S // inputs.P4_RANKS
+    g = inputs.p4_set()
+    q, k, v, wq, wk = (torch.from_numpy(np.ascontiguousarray(g[n])).cuda() for n in ("q", "k", "v", "w_q", "w_k"))
+    s4 = D ** -0.25
+    qn, kn = torch.empty_like(q), torch.empty_like(k)
+    out = {}
+    for name, Sq in (("p4_single", S), ("p4_rank", S_r)):
+        qs, qns = q[:, :Sq], qn[:, :Sq]
+        o = torch.empty((1, Sq, H, D), dtype=torch.float16, device="cuda")
+        lse = torch.empty((1, H, Sq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(cp.attn_fwd_workspace_size(1, H, Sq, S, D, cp.F16, cp.F16), dtype=torch.uint8,
+                         device="cuda")
+
+        def prologue():
+            cp.qk_rmsnorm(qs, wq, 1e-6, s4, out=qns, stream=stream)
+            cp.qk_rmsnorm(k, wk, 1e-6, s4, out=kn, stream=stream)
+
+        def attn():
+            cp.attn_fwd_ex(qns, kn, v, o=o, lse=lse, scale=1.0, workspace=ws, seq_major=True, stream=stream)
+
+        def layer():
+            prologue()
+            attn()
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(iters):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / iters
+
+        ms_layer, ms_attn, ms_pro = timed(layer), timed(attn), timed(prologue)
+        flops = 4.0 * H * Sq * S * D
+        out[f"{name}_ms"] = round(ms_layer, 3)
+        out[f"{name}_attn_tflops"] = round(flops / ms_attn / 1e9, 1)
+        out[f"{name}_prologue_ms"] = round(ms_pro, 3)
+        out[f"{name}_prologue_GBps"] = round(2 * 2 * (Sq + S) * H * D / ms_pro / 1e6, 1)
     return out
 
 

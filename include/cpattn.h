@@ -30,6 +30,10 @@
  *    into the running (O, LSE) by the attn_merge rule (first page, "Ring
  *    Attention").
  *
+ *  - qk_rmsnorm: the QK-RMSNorm prologue (fp32 RMSNorm over head_dim, cast
+ *    to the 16-bit type, split score scale) of the attention sample in
+ *    "TensorRT multi-device attention inference in practice", step 1.
+ *
  *  - ulysses_pack / ulysses_unpack: the sequence<->head relayout on either
  *    side of DeepSpeed Ulysses' two all-to-alls (first page, "DeepSpeed
  *    Ulysses"; 5520 tokens per rank at degree 8 in "Simplifying model
@@ -56,8 +60,8 @@
  *  - Functions are reentrant and thread-safe.  Calls on different streams
  *    may run concurrently as long as their buffers do not overlap.
  *
- * bf16 is the 16-bit brain-float format stored as raw 16-bit words; f32 is
- * IEEE binary32.
+ * bf16 is the 16-bit brain-float format stored as raw 16-bit words; f16 is
+ * IEEE binary16; f32 is IEEE binary32.
  */
 #ifndef CPATTN_H_
 #define CPATTN_H_
@@ -88,7 +92,7 @@ typedef enum {
 #define CPATTN_FLAG_ACCUMULATE 1u
 #define CPATTN_FLAG_SEQ_MAJOR 2u
 
-typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1 } cpattn_dtype;
+typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1, CPATTN_F16 = 2 } cpattn_dtype;
 
 typedef enum { CPATTN_SEQ_TO_HEAD = 0, CPATTN_HEAD_TO_SEQ = 1 } cpattn_dir;
 
@@ -109,8 +113,11 @@ typedef enum { CPATTN_SEQ_TO_HEAD = 0, CPATTN_HEAD_TO_SEQ = 1 } cpattn_dir;
  * dtypes: in_dtype = BF16 with o_dtype = BF16 (bf16 matrix cores, fp32
  * accumulation and softmax state, softmax weights rounded to bf16 for the PV
  * product, O rounded to nearest even) or o_dtype = F32 (the same computation
- * with O kept in f32, e.g. for ring partials); in_dtype = F32 requires
- * o_dtype = F32 (all arithmetic in f32).  Any other pair -> CPATTN_E_DTYPE.
+ * with O kept in f32, e.g. for ring partials); in_dtype = F16 with o_dtype =
+ * F16 or F32, the same with IEEE fp16 in place of bf16 (the precision of the
+ * attention sample in "TensorRT multi-device attention inference in
+ * practice"); in_dtype = F32 requires o_dtype = F32 (all arithmetic in f32).
+ * Any other pair -> CPATTN_E_DTYPE.
  *
  * o and lse must not overlap each other or q, k, v (CPATTN_E_ALIAS).
  */
@@ -139,15 +146,16 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
  * planned per call from the device's resident-workgroup count and limited
  * to what the workspace holds: (D + 1) * 1024 bytes per piece.
  * cpattn_attn_fwd_workspace_size gives the size the best plan uses;
- * less (or none) only means fewer (or no) pieces.  f32 inputs never split.
+ * less (or none) only means fewer (or no) pieces.  f32 inputs never split;
+ * bf16 and fp16 inputs share the plan.
  * Results differ from cpattn_attn_fwd's only by f32 rounding in the fold.
  *
  * CPATTN_FLAG_ACCUMULATE.  (o, lse) hold on entry the result of attention
  * over a disjoint key set (O normalised, f32; LSE natural; LSE = -inf with
  * O = 0 for "nothing yet"), and on return the result over the union:
  * each row is folded with the attn_merge rule in f32.  Requires in_dtype =
- * BF16 and o_dtype = F32 (else CPATTN_E_DTYPE).  With Skv = 0 the call
- * leaves (o, lse) unchanged.
+ * BF16 or F16 and o_dtype = F32 (else CPATTN_E_DTYPE).  With Skv = 0 the
+ * call leaves (o, lse) unchanged.
  *
  * CPATTN_FLAG_SEQ_MAJOR.  q, k, v and o are sequence-major (token-major):
  * q [B, Sq, H, D], k and v [B, Skv, H, D], o [B, Sq, H, D]; lse stays
@@ -195,7 +203,8 @@ cpattn_status cpattn_attn_fwd_split_plan(int64_t B, int64_t H, int64_t Sq, int64
  *   L   = M + ln(exp(La - M) + exp(Lb - M))
  *   O   = exp(La - L) * Oa + exp(Lb - L) * Ob
  *
- * computed in f32 and stored in o_dtype (bf16 rounded to nearest even).
+ * computed in f32 and stored in o_dtype (BF16, F16 or F32; 16-bit types
+ * rounded to nearest even).
  * An empty side (LSE = -inf, O = 0) is the identity; two empty sides give
  * O = 0, LSE = -inf.  o_out may be exactly o_a or exactly o_b, and lse_out
  * exactly lse_a or lse_b (in-place accumulation); any other overlap is
@@ -263,6 +272,29 @@ cpattn_status cpattn_ulysses_pack(const void* src, void* dst, int64_t B, int64_t
 cpattn_status cpattn_ulysses_unpack(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H,
                                     int64_t D, int64_t P, cpattn_dtype dt, cpattn_dir dir,
                                     hipStream_t stream);
+
+/*
+ * QK-RMSNorm prologue of the attention sample ("TensorRT multi-device
+ * attention inference in practice", step 1): per row of D values
+ *
+ *   y = round16( round16( x * rsqrt(mean(x^2) + eps) * w ) * round16(post_scale) )
+ *
+ * with the norm evaluated in f32 and round16 the rounding to dt (nearest,
+ * ties to even).  The page multiplies Q and K each by (1/D)^(1/4) after the
+ * cast; pass that as post_scale, or 1 for the plain RMSNorm (multiplying by 1
+ * is exact).
+ *
+ *   x, y   [rows, D]  dt (BF16 or F16; else CPATTN_E_DTYPE); any layout whose
+ *          rows of D are contiguous, e.g. [B, S, H, D] with rows = B*S*H
+ *   w      [D]        dt
+ *
+ * D a power of two in [8, 512] (CPATTN_E_HEADDIM); rows >= 1; eps finite and
+ * >= 0, post_scale finite and > 0 and representable after rounding to dt
+ * (CPATTN_E_SCALE).  y may be exactly x (in place); any other overlap of y
+ * with x or w is CPATTN_E_ALIAS.
+ */
+cpattn_status cpattn_qk_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int64_t D,
+                                float eps, float post_scale, cpattn_dtype dt, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* cpattn_status_string(cpattn_status s);

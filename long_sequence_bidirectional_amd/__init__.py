@@ -11,6 +11,7 @@ torch provides device memory and streams.
   attn_fwd_split_plan(B, H, Sq, Skv, D, slots, ws_bytes)  -> (split_tiles, pieces, bytes)
   attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None) -> (o_out, lse_out)
   ring_attn_fwd(q, k_chunks, v_chunks, ...)               -> (o, lse)
+  qk_rmsnorm(x, w, eps=1e-6, post_scale=1.0, out=None)   -> out
   ulysses_pack(src, P, direction, dst=None)               -> dst
   ulysses_unpack(src, P, direction, dst=None)             -> dst
 """
@@ -19,10 +20,11 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import (BF16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD, CpattnError, check,
+from ._lib import (BF16, F16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD, CpattnError, check,
                    lib)
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge",
+           "qk_rmsnorm", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
            "SEQ_TO_HEAD", "HEAD_TO_SEQ", "CpattnError", "lib"]
 
 
@@ -35,9 +37,11 @@ def _dtype_code(t):
     torch = _torch()
     if t.dtype == torch.bfloat16:
         return BF16
+    if t.dtype == torch.float16:
+        return F16
     if t.dtype == torch.float32:
         return F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float16 or float32)")
 
 
 def _dev(t, name):
@@ -173,6 +177,23 @@ def ring_attn_fwd(q, k_chunks, v_chunks, o=None, lse=None, o_work=None, lse_work
                                     B, H, Sq, Skv_c, n, D, float(scale), _stream(stream))
     check("cpattn_ring_attn_fwd", st)
     return o, lse
+
+
+def qk_rmsnorm(x, w, eps=1e-6, post_scale=1.0, out=None, stream=None):
+    """RMSNorm over the last dim of x (bf16 or fp16) times w, rounded to x's type, then times the
+    16-bit constant post_scale and rounded again; out may be x (in place)."""
+    D = x.shape[-1]
+    if w.shape != (D,) or w.dtype != x.dtype:
+        raise ValueError(f"w must be [{D}] of {x.dtype}")
+    if out is None:
+        out = _torch().empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    rows = x.numel() // D
+    st = lib().cpattn_qk_rmsnorm(_dev(x, "x"), _dev(w, "w"), _dev(out, "out"), rows, D, float(eps),
+                                 float(post_scale), _dtype_code(x), _stream(stream))
+    check("cpattn_qk_rmsnorm", st)
+    return out
 
 
 def _relayout_shapes(src, P, direction, pack):

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libcpattn.so")
 
 # enum values of include/cpattn.h
 OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_ALIGN, E_ALIAS, E_HIP, E_SCALE, E_FLAGS = range(10)
-BF16, F32 = 0, 1
+BF16, F32, F16 = 0, 1, 2
 SEQ_TO_HEAD, HEAD_TO_SEQ = 0, 1
 ABI_VERSION = 2
 FLAG_ACCUMULATE = 1
@@ -34,6 +34,7 @@ SIGNATURES = [
     ("cpattn_attn_fwd_split_plan", _E, [_I64, _I64, _I64, _I64, _I64, _I64, _U64, _PI64, _PI64, _PU64]),
     ("cpattn_attn_merge", _E, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _E, _P]),
     ("cpattn_ring_attn_fwd", _E, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _F, _P]),
+    ("cpattn_qk_rmsnorm", _E, [_P, _P, _P, _I64, _I64, _F, _F, _E, _P]),
     ("cpattn_ulysses_pack", _E, [_P, _P, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),
     ("cpattn_ulysses_unpack", _E, [_P, _P, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),
     ("cpattn_status_string", ctypes.c_char_p, [_E]),

@@ -6,8 +6,10 @@ The library is always rebuilt when this runs.
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 import time
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -17,7 +19,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libcpattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "merge.hip", "relayout.hip"]
+SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_fwd_f32.hip", "merge.hip", "relayout.hip",
+           "qk_norm.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared", "-fvisibility=hidden",
@@ -27,18 +30,37 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
-    t0 = time.time()
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
-    os.replace(tmp, LIB_PATH)
+    return res.stderr
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every translation unit in parallel, then link the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    t0 = time.time()
+    tmpdir = tempfile.mkdtemp(prefix="cpattn_build_")
+    try:
+        compile_flags = [f for f in FLAGS if f != "-shared"]
+        jobs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            jobs.append((obj, [HIPCC, *compile_flags, *extra_flags, "-I", os.path.join(ROOT, "include"), "-c",
+                               os.path.join(CSRC, src), "-o", obj]))
+        workers = min(len(jobs), max(1, min(os.cpu_count() or 1, 16)))
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            logs = list(pool.map(lambda j: _run(j[1]), jobs))
+        tmp = LIB_PATH + f".tmp{os.getpid()}"
+        logs.append(_run([HIPCC, *FLAGS, *extra_flags, "-o", tmp, *[o for o, _ in jobs]]))
+        os.replace(tmp, LIB_PATH)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     if verbose:
-        noise = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+        noise = [l for log in logs for l in log.splitlines() if "packed-fp32-ops" not in l and l.strip()]
         if noise:
             sys.stderr.write("\n".join(noise) + "\n")
         print(f"built {LIB_PATH} in {time.time() - t0:.1f}s")

@@ -2,6 +2,7 @@
 // and dispatch to the gfx950 kernels.  Semantics are documented in
 // include/cpattn.h.
 #include <math.h>
+#include <string.h>
 
 #include <algorithm>
 #include <atomic>
@@ -49,8 +50,13 @@ bool overlap(Range a, Range b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-int64_t dtype_size(cpattn_dtype t) { return t == CPATTN_BF16 ? 2 : 4; }
-bool dtype_valid(int t) { return t == CPATTN_BF16 || t == CPATTN_F32; }
+int64_t dtype_size(cpattn_dtype t) { return t == CPATTN_F32 ? 4 : 2; }
+bool dtype_valid(int t) { return t == CPATTN_BF16 || t == CPATTN_F32 || t == CPATTN_F16; }
+bool dtype_16bit(int t) { return t == CPATTN_BF16 || t == CPATTN_F16; }
+
+cpattn::MergeOut merge_out(cpattn_dtype t) {
+    return t == CPATTN_F32 ? cpattn::MergeOut::F32 : t == CPATTN_F16 ? cpattn::MergeOut::F16 : cpattn::MergeOut::BF16;
+}
 
 bool dims_ok(std::initializer_list<int64_t> xs, int64_t min_value) {
     for (int64_t x : xs)
@@ -185,7 +191,7 @@ cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, flo
     a.split_tiles = 0;
     a.split_pieces = 1;
     a.stream = stream;
-    if (in_dtype != CPATTN_BF16) return hip_status(cpattn::launch_attn_fwd_f32(a));
+    if (in_dtype == CPATTN_F32) return hip_status(cpattn::launch_attn_fwd_f32(a));
     if (ws_o && ws_lse && ws_pieces > 0) {
         const SplitPlan p = plan_split(BH, Sq, Skv, D, device_slots(D, a.out_f32),
                                        (uint64_t)ws_pieces * piece_bytes(D));
@@ -196,7 +202,7 @@ cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, flo
             a.ws_lse = ws_lse;
         }
     }
-    return hip_status(cpattn::launch_attn_fwd_bf16(a));
+    return hip_status(in_dtype == CPATTN_F16 ? cpattn::launch_attn_fwd_f16(a) : cpattn::launch_attn_fwd_bf16(a));
 }
 
 struct AttnFwdCheck {
@@ -210,7 +216,7 @@ cpattn_status check_attn_fwd(const void* q, const void* k, const void* v, void* 
                              cpattn_dtype o_dtype, AttnFwdCheck* out) {
     if (!q || !o || !lse || (Skv != 0 && (!k || !v))) return CPATTN_E_NULL;
     if (!dtype_valid(in_dtype) || !dtype_valid(o_dtype)) return CPATTN_E_DTYPE;
-    if (in_dtype == CPATTN_F32 && o_dtype != CPATTN_F32) return CPATTN_E_DTYPE;
+    if (o_dtype != in_dtype && o_dtype != CPATTN_F32) return CPATTN_E_DTYPE;   // O in the input type or f32
     AttnCheck& c = out->c;
     const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, scale, 32, &c);
     if (st != CPATTN_OK) return st;
@@ -252,7 +258,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, con
     AttnFwdCheck ck;
     const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, &ck);
     if (st != CPATTN_OK) return st;
-    if (acc && (in_dtype != CPATTN_BF16 || o_dtype != CPATTN_F32)) return CPATTN_E_DTYPE;
+    if (acc && (!dtype_16bit(in_dtype) || o_dtype != CPATTN_F32)) return CPATTN_E_DTYPE;
     if (workspace_bytes != 0 && !workspace) return CPATTN_E_NULL;
     int64_t ws_pieces = 0;
     float *ws_o = nullptr, *ws_lse = nullptr;
@@ -297,7 +303,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_workspace_size(int64_t B, int64_t H,
     const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, 1.0f, 32, &c);
     if (st != CPATTN_OK) return st;
     *bytes = 0;
-    if (in_dtype != CPATTN_BF16) return CPATTN_OK;
+    if (!dtype_16bit(in_dtype)) return CPATTN_OK;
     const int64_t slots = device_slots(D, o_dtype == CPATTN_F32);
     if (slots <= 0) return CPATTN_E_HIP;
     *bytes = plan_split(B * H, Sq, Skv, D, slots, UINT64_MAX).bytes;
@@ -326,7 +332,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_
     if ((lse_out != lse_a && overlap(lo, la)) || (lse_out != lse_b && overlap(lo, lb))) return CPATTN_E_ALIAS;
     if (overlap(ro, la) || overlap(ro, lb) || overlap(ro, lo) || overlap(lo, ra) || overlap(lo, rb))
         return CPATTN_E_ALIAS;
-    cpattn::MergeArgs m{o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, D, o_dtype == CPATTN_F32, stream};
+    cpattn::MergeArgs m{o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, D, merge_out(o_dtype), stream};
     return hip_status(cpattn::launch_attn_merge(m));
 }
 
@@ -404,6 +410,39 @@ CPATTN_EXPORT cpattn_status cpattn_ulysses_unpack(const void* src, void* dst, in
                                                   int64_t H, int64_t D, int64_t P, cpattn_dtype dt,
                                                   cpattn_dir dir, hipStream_t stream) {
     return relayout(src, dst, B, S_local, H, D, P, dt, dir, false, stream);
+}
+
+namespace {
+
+// Host-side rounding of a float to the 16-bit types (nearest, ties to even).
+float round_to_f16_host(float x) { return (float)(_Float16)x; }
+float round_to_bf16_host(float x) {
+    uint32_t b;
+    memcpy(&b, &x, 4);
+    b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+    float r;
+    memcpy(&r, &b, 4);
+    return r;
+}
+
+}  // namespace
+
+CPATTN_EXPORT cpattn_status cpattn_qk_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int64_t D,
+                                              float eps, float post_scale, cpattn_dtype dt, hipStream_t stream) {
+    if (!x || !w || !y) return CPATTN_E_NULL;
+    if (!dtype_16bit(dt)) return CPATTN_E_DTYPE;
+    if (D < 8 || D > 512 || (D & (D - 1)) != 0) return CPATTN_E_HEADDIM;
+    if (rows < 1 || rows > kMaxDim / (D / 8)) return CPATTN_E_SHAPE;   // one thread per 16 bytes
+    if (!(eps >= 0.f) || !isfinite(eps) || !(post_scale > 0.f) || !isfinite(post_scale)) return CPATTN_E_SCALE;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return CPATTN_E_ALIGN;
+    const int64_t bytes = rows * D * 2;
+    const Range rx = range(x, bytes), ry = range(y, bytes), rw = range(w, D * 2);
+    if ((y != x && overlap(rx, ry)) || overlap(rw, ry)) return CPATTN_E_ALIAS;
+    const bool f16 = dt == CPATTN_F16;
+    const float s16 = f16 ? round_to_f16_host(post_scale) : round_to_bf16_host(post_scale);
+    if (!(s16 > 0.f) || !isfinite(s16)) return CPATTN_E_SCALE;   // underflows or overflows the 16-bit type
+    cpattn::QkNormArgs a{x, w, y, rows, D, eps, s16, post_scale != 1.0f, f16, stream};
+    return hip_status(cpattn::launch_qk_rmsnorm(a));
 }
 
 CPATTN_EXPORT const char* cpattn_status_string(cpattn_status s) {

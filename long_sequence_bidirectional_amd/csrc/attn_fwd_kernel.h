@@ -1,0 +1,504 @@
+// Non-causal attention forward on the 16-bit matrix cores of gfx950 (bf16 or fp16 inputs).
+//
+// Kernel template shared by the bf16 and fp16 instantiation units.
+//
+// Computes, per (b, h) and query row i, the online-softmax form of
+//   O_i = sum_j softmax_j(scale * q_i . k_j) v_j,   LSE_i = ln sum_j exp(scale * q_i . k_j)
+// streaming K/V in blocks of BN keys, as Ring Attention's blockwise online
+// softmax does ("Scaling AI inference across multiple GPUs using NVIDIA
+// TensorRT with multi-device inference support", section "Ring Attention";
+// no causal mask, section "Context parallelism").
+//
+// Work split.  One workgroup = 8 wave64s = one tile of 256 query rows of one
+// (b, h); wave w owns rows [32w, 32w+32) of the tile.
+//
+// Transposed formulation.  Each wave computes S^T = K Q^T and O^T = V^T P^T
+// with v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane
+// holds one column, so with queries on the column axis every lane owns one
+// query row: the row max is lane-local apart from one exchange between the
+// two 32-lane halves, the row sum needs no exchange until the epilogue, the
+// softmax weights P^T come out of the S^T accumulator already laid out as the
+// B operand of the PV product (no LDS round trip for P), and the rescale of O
+// is a per-lane scalar.
+//
+//   S^T tile (32 keys x 32 queries):  lane l, register i holds
+//       key (i/4)*8 + (l/32)*4 + i%4,  query l%32.
+//   PV k-step t covers the 16 keys 16t..16t+15 of the block; lane half h
+//   supplies slots (h, 0..7) = S^T registers 8*(t%2)..+7 of key tile t/2,
+//   i.e. keys 16t + 8*(j/4) + 4h + j%4.
+//
+// Registers and LDS.  Each wave keeps its Q^T operand (32 rows x D) in
+// registers for the whole tile.  K and V blocks (three buffers each) are stored
+// in LDS row-major with 16-byte chunks XOR-swizzled per row and filled by direct
+// global->LDS loads (global_load_lds_dwordx4: lane i writes bytes 16i..16i+15
+// of a 1 KB piece, so a wave's load is a plain copy and needs no registers).
+// The V^T A-operand of the PV product comes from two ds_read_b64_tr_b16 per
+// MFMA: in each 16-lane group, lane L points at row kv0 + L/4, columns
+// d0 + 4(L%4) .. +3 and receives V[kv0 .. kv0+3][d0 + L], i.e. four keys of
+// one head-dim column -- exactly the per-lane k-slots above.  The swizzles
+// make the K reads (16 rows x one chunk) and the V transposing reads
+// (4 rows x 4 chunks) hit 64 distinct banks.
+//
+// Schedule.  Per key block j a wave runs an MFMA slot M_j = {S_j = K_j Q^T,
+// O += V_{j-1} P_{j-1}} and a softmax slot SM_j (max, exp2, row sum, bf16
+// weights, rescale of O when needed).  Waves w and w+4 share a SIMD; group 1
+// (waves 4-7) runs one slot behind group 0, so on every SIMD one wave issues
+// MFMAs while the other computes exponentials, with one workgroup barrier
+// per slot.  In an MFMA slot the operand reads run three MFMAs ahead.  Global
+// loads are issued from softmax slots, two slots before their data is needed
+// (three K/V buffers), and the slot barriers are plain s_barrier: each wave
+// waits only for its own older loads (vmcnt) before arriving.
+//
+// Softmax in base 2: t = s * scale * log2(e), p = exp2(t - m), natural
+// LSE = (m + log2 l) * ln 2.  The running max m is only raised when a block's
+// max exceeds it by more than 2^8 (so p <= 256); otherwise the stale m is kept
+// and O needs no rescale.  The result is exact after the final division by l
+// because every term of O and l carries the same factor 2^-m.  Keys past Skv
+// in the last block get -inf.  Out-of-range rows are loaded clamped to the
+// last valid row (finite values that get weight 0 or are never stored).
+#pragma once
+
+#include <utility>
+
+#include "common.h"
+#include "kernels.h"
+
+#ifndef CPATTN_AI
+#define CPATTN_AI __attribute__((always_inline))
+#endif
+
+namespace cpattn {
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T*)(p))
+
+constexpr int kBM = kAttnTileRows;    // query rows per workgroup (8 waves x 32)
+constexpr int kBN = 64;               // keys per block
+constexpr int kReadAhead = 3;         // MFMA operand reads issued this many MFMAs ahead
+constexpr int NBUF = 3;               // K and V buffers in LDS
+constexpr float kRescaleTh = 8.0f;    // raise m only when the block max exceeds it by > 2^8
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Chunk c of row r is stored at chunk position c ^ swz(r).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {     // K and Q: 16 consecutive rows, same chunk
+    constexpr int RPB = 256 / (2 * D);            // rows per 256-byte bank row
+    return (r / RPB) % (D / 8);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {     // V: 4 consecutive rows x 4 chunks
+    constexpr int RPB = 256 / (2 * D);
+    return 4 * ((r / RPB) % (D / 32));
+}
+
+// One v_mfma_f32_32x32x16 of the input type: D(32x32) += A(32x16) B(16x32).
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+}
+
+// Two fp32 -> one packed pair of the input type, round to nearest even.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
+    if constexpr (F16) return pack_f16x2(lo, hi);
+    else return pack_bf16x2(lo, hi);
+}
+
+template <int D, bool F16, bool OUT_F32, bool SEQ>
+__global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
+    Strides so, AttnTileMap map, float c) {
+    constexpr int BN = kBN;
+    constexpr int NC = D / 8;               // 16-byte chunks per row
+    constexpr int NKS = D / 16;             // k-steps of the QK^T product
+    constexpr int NDT = D / 32;             // 32-wide d tiles of O^T
+    constexpr int NKT = BN / 32;            // 32-key tiles of S^T per block
+    constexpr int NPB = BN / 16;            // 16-key k-steps of the PV product
+    constexpr int BLK_BYTES = BN * D * 2;
+    constexpr int LOADS_PER_WAVE = BLK_BYTES / 1024 / 8;
+    constexpr int ROWS_PER_LOAD = 1024 / (2 * D);
+    constexpr int NQK = NKT * NKS;          // MFMA jobs of S = K Q^T
+    constexpr int NPV = NDT * NPB;          // MFMA jobs of O += V^T P^T
+    static_assert(LOADS_PER_WAVE >= 1, "block too small for the loader");
+
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks[NBUF][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs[NBUF][BN * D];
+
+    // Work unit of this workgroup.  Workgroup ids are dealt round-robin over the
+    // XCDs; both parts of the grid are mapped so that each XCD walks a contiguous
+    // range of units, i.e. the workgroups resident on one XCD share a head and
+    // its K/V stream in L2.  Ids below grid_dp run whole tiles [0, n_dp); the
+    // rest run key-range pieces of tiles [n_dp, n_dp + n_split), piece-major so
+    // that neighbours read the same keys.  A piece p of s covers key blocks
+    // [p*nblk/s, (p+1)*nblk/s) and leaves a normalised f32 partial and its LSE
+    // in workspace slot (tile - n_dp) * s + p.
+    const int bid = blockIdx.x;
+    const int nblk_all = (Skv_all + BN - 1) / BN;
+    int tile, kb0 = 0, slot = -1, nblk = nblk_all;
+    if (bid < map.grid_dp) {
+        const int logical = (bid % kNumXcd) * map.per_xcd_dp + bid / kNumXcd;
+        if (logical >= map.n_dp) return;
+        tile = logical;
+    } else {
+        const int u = bid - map.grid_dp;
+        const int logical = (u % kNumXcd) * map.per_xcd_sp + u / kNumXcd;
+        if (logical >= map.n_split * map.split_s) return;
+        const int p = logical / map.n_split;
+        const int ti = logical - p * map.n_split;
+        tile = map.n_dp + ti;
+        slot = ti * map.split_s + p;
+        kb0 = (int)((int64_t)p * nblk_all / map.split_s);
+        nblk = (int)((int64_t)(p + 1) * nblk_all / map.split_s) - kb0;
+    }
+    const int Skv = min(Skv_all - kb0 * BN, nblk * BN);   // keys of this unit
+    const int bh = tile / nQt;
+    const int qt = tile - bh * nQt;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int L16 = lane & 15;
+    const int g16 = (lane >> 4) & 1;
+    const int group = wave >> 2;            // waves w and w+4 share a SIMD
+
+    // Row strides: D for head-major operands (compile time), runtime for sequence-major ones.
+    const int64_t q_row = SEQ ? sq.row : D, kv_row = SEQ ? skv.row : D, o_row = SEQ ? so.row : D;
+    const int b = SEQ ? bh / H : 0, h = SEQ ? bh - b * H : 0;
+    const int64_t q_base = SEQ ? b * sq.batch + h * sq.head : (int64_t)bh * Sq * D;
+    const int64_t o_base = SEQ ? b * so.batch + h * so.head : (int64_t)bh * Sq * D;
+    const int64_t kv_off = (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv_all * D) + (int64_t)kb0 * BN * kv_row;
+    const uint16_t* qp = q + q_base;
+    const uint16_t* kp = k + kv_off;
+    const uint16_t* vp = v + kv_off;
+    const int qrow = qt * kBM + wave * 32 + l32;
+
+    // ---- direct global -> LDS loads of K/V blocks (rows clamped to the last valid one)
+    auto load_block = [&](const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
+        uint16_t* base = dst + wave * LOADS_PER_WAVE * 512;
+        auto one = [&]<int I>(ic<I>) CPATTN_AI {
+            const int row = (wave * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
+            const int ch = (lane % NC) ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+            const int r = min(j * BN + row, Skv - 1);
+            const char* g = reinterpret_cast<const char*>(src + r * kv_row + ch * 8) - I * 1024;
+            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, g), LDS_PTR(void, base), 16, I * 1024, 0);
+        };
+        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI { (one(ic<Is>{}), ...); }(
+            std::make_integer_sequence<int, LOADS_PER_WAVE>{});
+    };
+    auto wait_loads = [&]() CPATTN_AI { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+    // Q^T operand of this wave, held in registers for the whole tile: for k-step ks lane
+    // (l32, hh) holds q[row l32][16 ks + 8 hh .. +7], read straight from global memory
+    // (rows past Sq clamped to the last valid one).
+    u32x4 qreg[NKS];
+    {
+        const uint16_t* qr = qp + min(qrow, Sq - 1) * q_row + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qreg[ks] = *reinterpret_cast<const u32x4*>(qr + 16 * ks);
+    }
+
+    // ---- LDS read addresses: lane-dependent parts (elements); the rest folds into offsets
+    int koff[NKS], voff[NDT];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * D + (((2 * ks + hh) ^ swz_k<D>(l32)) * 8);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        const int col = dt * 32 + 16 * g16 + 4 * (L16 & 3);
+        const int row = 4 * hh + (L16 >> 2);
+        voff[dt] = row * D + (((col >> 3) ^ swz_v<D>(row)) * 8) + ((col >> 2) & 1) * 4;
+    }
+    auto read_k = [&]<int BUF>(ic<BUF>, int kt, int ks) CPATTN_AI -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(&Ks[BUF][kt * 32 * D + koff[ks]]);
+    };
+    auto read_vt = [&]<int BUF>(ic<BUF>, int dt, int t) CPATTN_AI -> u32x4 {
+        i16x4 r[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+            r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDS_PTR(i16x4, &Vs[BUF][(16 * t + 8 * h2) * D + voff[dt]]));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, r[0]), a1 = __builtin_bit_cast(u32x2, r[1]);
+        return u32x4{a0[0], a0[1], a1[0], a1[1]};
+    };
+
+    // ---- per-wave state
+    f32x16 oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+    f32x16 s[NKT];             // S_j^T
+    u32x4 pb[NPB];             // P_j^T as the B operand of the PV product
+    float m_run = -INFINITY;   // running max, base-2 units (scale*log2e applied)
+    float l_run = 0.f;         // this lane half's partial row sum
+    float alpha = 1.f;
+
+    // MFMA slot body: the job list [QK jobs in (ks, kt) order] ++ [PV jobs in (t, dt)
+    // order] (consecutive jobs use different accumulators), operand reads kReadAhead
+    // jobs ahead, fenced so the compiler keeps that distance.
+    auto mfma_jobs = [&]<int KB, int VB, bool QK, bool PV>(ic<KB>, ic<VB>, std::bool_constant<QK>,
+                                                           std::bool_constant<PV>) CPATTN_AI {
+        constexpr int J0 = QK ? 0 : NQK;
+        constexpr int J1 = PV ? NQK + NPV : NQK;
+        constexpr int NJ = J1 - J0;
+        if constexpr (QK) {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+        }
+        u32x4 frag[NJ];
+        auto rd = [&]<int I>(ic<I>) CPATTN_AI {
+            constexpr int jid = J0 + I;
+            if constexpr (jid < NQK) {
+                constexpr int kt = jid % NKT, ks = jid / NKT;
+                frag[I] = read_k(ic<KB>{}, kt, ks);
+            } else {
+                constexpr int p = jid - NQK;
+                frag[I] = read_vt(ic<VB>{}, p % NDT, p / NDT);
+            }
+        };
+        auto step = [&]<int I>(ic<I>) CPATTN_AI {
+            if constexpr (I + kReadAhead < NJ) rd(ic<I + kReadAhead>{});
+            constexpr int jid = J0 + I;
+            if constexpr (jid < NQK) {
+                constexpr int kt = jid % NKT, ks = jid / NKT;
+                s[kt] = mfma16<F16>(frag[I], qreg[ks], s[kt]);
+            } else {
+                constexpr int p = jid - NQK, dt = p % NDT, t = p / NDT;
+                oacc[dt] = mfma16<F16>(frag[I], pb[t], oacc[dt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI {
+            (rd(ic<Is>{}), ...);
+        }(std::make_integer_sequence<int, (kReadAhead < NJ ? kReadAhead : NJ)>{});
+        __builtin_amdgcn_sched_barrier(0);
+        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI {
+            (step(ic<Is>{}), ...);
+        }(std::make_integer_sequence<int, NJ>{});
+    };
+    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1), with P = j & 1.
+    auto M = [&]<int R>(ic<R>, int j) CPATTN_AI {   // R = j % 3
+        constexpr int KB = R, VB = (R + 2) % 3;
+        __builtin_amdgcn_s_setprio(1);
+        if (j < nblk && j >= 1) mfma_jobs(ic<KB>{}, ic<VB>{}, std::true_type{}, std::true_type{});
+        else if (j < nblk) mfma_jobs(ic<KB>{}, ic<VB>{}, std::true_type{}, std::false_type{});
+        else if (j >= 1) mfma_jobs(ic<KB>{}, ic<VB>{}, std::false_type{}, std::true_type{});
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // SM_j: softmax of S_j -> P_j, row statistics, O *= alpha_j when some row raised its max.
+    auto SM = [&](int j) CPATTN_AI {
+        if (j == nblk - 1 && (Skv % BN) != 0) {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = j * BN + kt * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+                    if (key >= Skv) s[kt][i] = -INFINITY;
+                }
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+        mx = max_across_halves(mx) * c;
+        const bool raise = mx > m_run + kRescaleTh;
+        const float m_new = raise ? mx : m_run;
+        alpha = exp2_fast(m_run - m_new);   // 1 when not raised; 0 on the first block
+        m_run = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    p[e] = exp2_fast(__builtin_fmaf(s[kt][half * 8 + e], c, -m_new));
+                    psum += p[e];
+                }
+                pb[kt * 2 + half] = u32x4{pack16x2<F16>(p[0], p[1]), pack16x2<F16>(p[2], p[3]),
+                                          pack16x2<F16>(p[4], p[5]), pack16x2<F16>(p[6], p[7])};
+            }
+        l_run = l_run * alpha + psum;
+        // keep the row sum and the packed weights materialised in this slot (otherwise
+        // the compiler defers them past the barrier and holds every weight live)
+        asm volatile("" : "+v"(l_run));
+#pragma unroll
+        for (int t = 0; t < NPB; ++t) asm volatile("" : "+v"(pb[t]));
+        if (__ballot(raise) != 0) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        }
+    };
+    // loads issued at global slot 2j: K_{j+2} and V_{j+1} (into the buffers M_{j-1} released)
+    auto issue = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        if (j + 2 < nblk) load_block(kp, Ks[(R + 2) % 3], j + 2, false);
+        if (j + 1 < nblk) load_block(vp, Vs[(R + 1) % 3], j + 1, true);
+    };
+    // Wait until at most this wave's latest issue of loads (issue(jl)) is in flight.  The
+    // count is exact only when that issue was a full one (K and V); near the end, where it
+    // carried fewer loads, wait for everything.
+    auto wait_older = [&](int jl) CPATTN_AI {
+        if (jl + 2 < nblk)
+            asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS_PER_WAVE) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    load_block(kp, Ks[0], 0, false);
+    if (nblk > 1) load_block(kp, Ks[1], 1, false);
+    load_block(vp, Vs[0], 0, true);
+    wait_loads();
+    __syncthreads();
+
+    // Both groups run M_0, SM_0, M_1, SM_1, ..., M_nblk; group 1 starts one slot late (an
+    // extra barrier up front; group 0 adds one at the end).  Each wave issues its share of
+    // (K_{j+2}, V_{j+1}) at the start of a softmax slot -- group 1 at global slot 2j, group 0
+    // at 2j+1 -- into the buffers last read by M_{j-1} (slots 2j-2, 2j-1).  Before the
+    // barrier ending a softmax slot a wave waits for all but its latest issue, so both
+    // shares are in LDS by the end of slot 2j+3, in time for M_{j+2} (slot 2j+4).  The slot
+    // barrier itself does not wait for outstanding memory operations.
+    auto slot_barrier = [&]() CPATTN_AI { asm volatile("s_barrier" ::: "memory"); };
+    auto body = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        M(ic<R>{}, j);
+        __builtin_amdgcn_sched_barrier(0);
+        slot_barrier();
+        if (group != 0) issue(ic<(R + 1) % 3>{}, j + 1);
+        else issue(ic<R>{}, j);
+        if (j < nblk) SM(j);
+        wait_older(group != 0 ? j + 1 : j);
+        __builtin_amdgcn_sched_barrier(0);
+        slot_barrier();
+    };
+    if (group != 0) {
+        issue(ic<0>{}, 0);
+        slot_barrier();
+    }
+    int j = 0;
+    for (; j + 2 <= nblk; j += 3) {
+        body(ic<0>{}, j);
+        body(ic<1>{}, j + 1);
+        body(ic<2>{}, j + 2);
+    }
+    if (j <= nblk) body(ic<0>{}, j);
+    if (j + 1 <= nblk) body(ic<1>{}, j + 1);
+    if (group == 0) slot_barrier();
+
+    // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2; a piece goes to the workspace, an
+    // accumulating call folds the result into the (O, LSE) already in o/lse.
+    const float l_tot = sum_across_halves(l_run);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const float lse_new = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (slot >= 0) {
+        const size_t wrow = (size_t)slot * kBM + wave * 32 + l32;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + g * 8 + hh * 4;
+                *reinterpret_cast<f32x4*>(map.ws_o + wrow * D + d0) =
+                    f32x4{oacc[dt][g * 4 + 0] * inv, oacc[dt][g * 4 + 1] * inv, oacc[dt][g * 4 + 2] * inv,
+                          oacc[dt][g * 4 + 3] * inv};
+            }
+        if (hh == 0) map.ws_lse[wrow] = lse_new;
+    } else if (qrow < Sq) {
+        const int64_t orow = o_base + qrow * o_row;
+        float wa = 0.f, wb = inv, L = lse_new;   // O = wa * O_old + wb * acc
+        if (OUT_F32 && map.accumulate) {
+            const float la = lse[(size_t)bh * Sq + qrow];
+            const float mx = fmaxf(la, lse_new);
+            wb = 0.f;
+            L = -INFINITY;
+            if (mx != -INFINITY) {
+                const float ea = expf(la - mx), eb = expf(lse_new - mx);
+                const float tot = ea + eb;
+                L = mx + logf(tot);
+                wa = ea / tot;
+                wb = eb / tot * inv;
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + g * 8 + hh * 4;
+                f32x4 x = f32x4{oacc[dt][g * 4 + 0], oacc[dt][g * 4 + 1], oacc[dt][g * 4 + 2],
+                                oacc[dt][g * 4 + 3]} * wb;
+                if constexpr (OUT_F32) {
+                    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0);
+                    if (map.accumulate) x += *dst * wa;
+                    *dst = x;
+                } else {
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + d0) =
+                        u32x2{pack16x2<F16>(x[0], x[1]), pack16x2<F16>(x[2], x[3])};
+                }
+            }
+        if (hh == 0) lse[(size_t)bh * Sq + qrow] = L;
+    }
+}
+
+template <int D, bool F16, bool OUT_F32, bool SEQ>
+hipError_t launch(const AttnFwdArgs& a) {
+    const int nQt = (int)((a.Sq + kBM - 1) / kBM);
+    const int64_t total = (int64_t)a.BH * nQt;
+    AttnTileMap m{};
+    m.n_dp = (int)(total - a.split_tiles);
+    m.per_xcd_dp = (m.n_dp + kNumXcd - 1) / kNumXcd;
+    m.grid_dp = m.per_xcd_dp * kNumXcd;
+    m.n_split = (int)a.split_tiles;
+    m.split_s = a.split_tiles > 0 ? (int)a.split_pieces : 1;
+    m.per_xcd_sp = (m.n_split * m.split_s + kNumXcd - 1) / kNumXcd;
+    m.ws_o = a.ws_o;
+    m.ws_lse = a.ws_lse;
+    m.accumulate = a.accumulate ? 1 : 0;
+    const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;
+    const float c = (float)((double)a.scale * 1.4426950408889634);
+    hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, F16, OUT_F32, SEQ>), dim3(grid), dim3(512), 0, a.stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)a.H, a.sq,
+                       a.skv, a.so, m, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.split_tiles == 0) return e;
+    MergePiecesArgs f{a.ws_o, a.ws_lse, a.o, a.lse, m.n_dp, m.n_split, m.split_s, nQt, a.H, a.so, a.Sq, a.D,
+                      a.out_f32 ? MergeOut::F32 : (F16 ? MergeOut::F16 : MergeOut::BF16), a.accumulate, a.stream};
+    return launch_merge_pieces(f);
+}
+
+template <int D, bool F16, bool OUT_F32>
+int occupancy() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_mfma_kernel<D, F16, OUT_F32, false>, 512, 0) !=
+        hipSuccess)
+        return 0;
+    return n;
+}
+
+template <int D, bool F16, bool OUT_F32>
+hipError_t launch_layout(const AttnFwdArgs& a) {
+    return a.seq_major ? launch<D, F16, OUT_F32, true>(a) : launch<D, F16, OUT_F32, false>(a);
+}
+
+template <bool F16>
+hipError_t launch_any(const AttnFwdArgs& a) {
+    if (a.D == 128) return a.out_f32 ? launch_layout<128, F16, true>(a) : launch_layout<128, F16, false>(a);
+    return a.out_f32 ? launch_layout<64, F16, true>(a) : launch_layout<64, F16, false>(a);
+}
+
+}  // namespace
+}  // namespace cpattn

@@ -54,10 +54,14 @@ struct AttnTileMap {
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a);
+hipError_t launch_attn_fwd_f16(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a);
 
 // Resident workgroups per CU of the bf16 attention kernel (0 if the runtime cannot tell).
 int attn_fwd_bf16_blocks_per_cu(int64_t D, bool out_f32);
+
+// Storage type of a merged O.
+enum class MergeOut { BF16, F16, F32 };
 
 // Merge of the key-range pieces of split tiles (and, when accumulating, of the
 // (O, LSE) already in o/lse) into the final rows of o/lse.
@@ -74,7 +78,7 @@ struct MergePiecesArgs {
     Strides so;       // of o
     int64_t Sq;
     int64_t D;
-    bool out_f32;
+    MergeOut out;
     bool accumulate;
     hipStream_t stream;
 };
@@ -93,11 +97,28 @@ struct MergeArgs {
     float* lse_out;
     int64_t rows;    // B * H * S
     int64_t D;
-    bool f32;        // o dtype: f32 if true, bf16 otherwise
+    MergeOut o_type;
     hipStream_t stream;
 };
 
 hipError_t launch_attn_merge(const MergeArgs& a);
+
+// RMSNorm over rows of D 16-bit values, times w, rounded to the 16-bit type, then
+// (has_scale) times the 16-bit constant scale16 and rounded again.
+struct QkNormArgs {
+    const void* x;
+    const void* w;      // [D]
+    void* y;            // may be x
+    int64_t rows;
+    int64_t D;          // power of two, 8..512
+    float eps;
+    float scale16;      // already a value of the 16-bit type
+    bool has_scale;
+    bool f16;           // fp16 (else bf16)
+    hipStream_t stream;
+};
+
+hipError_t launch_qk_rmsnorm(const QkNormArgs& a);
 
 // Relayout modes (see cpattn.h): 0 pack seq->head, 1 unpack seq->head,
 // 2 pack head->seq, 3 unpack head->seq.

@@ -19,7 +19,23 @@
 namespace cpattn {
 namespace {
 
-template <bool F32>
+// Widen the low / high 16-bit halves of a packed pair of the 16-bit O type.
+template <MergeOut T>
+__device__ __forceinline__ float lo16(uint32_t w) {
+    if constexpr (T == MergeOut::F16) return f16_bits_to_f32(w & 0xFFFFu);
+    else return __uint_as_float(w << 16);
+}
+template <MergeOut T>
+__device__ __forceinline__ float hi16(uint32_t w) {
+    if constexpr (T == MergeOut::F16) return f16_bits_to_f32(w >> 16);
+    else return __uint_as_float(w & 0xFFFF0000u);
+}
+template <MergeOut T>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+    if constexpr (T == MergeOut::F16) return pack_f16x2(lo, hi);
+    else return pack_bf16x2(lo, hi);
+}
+
 __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, float& wb, float& L) {
     const float m = fmaxf(la, lb);
     wa = 0.f;
@@ -37,7 +53,7 @@ __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, flo
 
 // Fast path (D/8 <= 64): each wave owns MU groups of 64/(D/8) rows; every lane loads all of
 // its chunks (both operands, both LSEs) before computing and storing any of them.
-template <bool F32, int MU>
+template <MergeOut T, int MU>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const void* o_a, const float* lse_a, const void* o_b,
                                                          const float* lse_b, void* o_out, float* lse_out,
                                                          int64_t rows, int D, int rows_per_wave) {
@@ -47,6 +63,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* o_a, const 
     const int r_in = lane / tpr;
     if (r_in >= rows_per_wave) return;
     const int ch = lane - r_in * tpr;
+    constexpr bool F32 = T == MergeOut::F32;
     constexpr int NV = F32 ? 2 : 1;     // 16-byte vectors per 8-element chunk
     u32x4 a[MU][NV], b[MU][NV];
     float la[MU], lb[MU];
@@ -69,7 +86,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* o_a, const 
     for (int u = 0; u < MU; ++u) {
         if (row[u] >= rows) continue;
         float wa, wb, L;
-        merge_weights<F32>(la[u], lb[u], wa, wb, L);
+        merge_weights(la[u], lb[u], wa, wb, L);
         const size_t off = ((size_t)row[u] * D + (size_t)ch * 8) * (F32 ? 4 : 2) / 16;
         if constexpr (F32) {
 #pragma unroll
@@ -82,9 +99,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* o_a, const 
             u32x4 r;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const float alo = __uint_as_float(a[u][0][w] << 16), ahi = __uint_as_float(a[u][0][w] & 0xFFFF0000u);
-                const float blo = __uint_as_float(b[u][0][w] << 16), bhi = __uint_as_float(b[u][0][w] & 0xFFFF0000u);
-                r[w] = pack_bf16x2(__builtin_fmaf(alo, wa, blo * wb), __builtin_fmaf(ahi, wa, bhi * wb));
+                const float alo = lo16<T>(a[u][0][w]), ahi = hi16<T>(a[u][0][w]);
+                const float blo = lo16<T>(b[u][0][w]), bhi = hi16<T>(b[u][0][w]);
+                r[w] = pack16<T>(__builtin_fmaf(alo, wa, blo * wb), __builtin_fmaf(ahi, wa, bhi * wb));
             }
             __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(o_out) + off);
         }
@@ -93,15 +110,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* o_a, const 
 }
 
 // General path (D/8 > 64): one row per wave, lanes loop over the row's chunks.
-template <bool F32>
+template <MergeOut T>
 __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const void* o_a, const float* lse_a, const void* o_b,
                                                               const float* lse_b, void* o_out, float* lse_out,
                                                               int64_t rows, int D) {
     const int lane = threadIdx.x & 63;
     const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (row >= rows) return;
+    constexpr bool F32 = T == MergeOut::F32;
     float wa, wb, L;
-    merge_weights<F32>(lse_a[row], lse_b[row], wa, wb, L);
+    merge_weights(lse_a[row], lse_b[row], wa, wb, L);
     const int tpr = D >> 3;
     for (int ch = lane; ch < tpr; ch += 64) {
         const size_t off = (size_t)row * D + (size_t)ch * 8;
@@ -118,9 +136,9 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const void* o_a, c
             u32x4 r;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const float alo = __uint_as_float(a[w] << 16), ahi = __uint_as_float(a[w] & 0xFFFF0000u);
-                const float blo = __uint_as_float(b[w] << 16), bhi = __uint_as_float(b[w] & 0xFFFF0000u);
-                r[w] = pack_bf16x2(__builtin_fmaf(alo, wa, blo * wb), __builtin_fmaf(ahi, wa, bhi * wb));
+                const float alo = lo16<T>(a[w]), ahi = hi16<T>(a[w]);
+                const float blo = lo16<T>(b[w]), bhi = hi16<T>(b[w]);
+                r[w] = pack16<T>(__builtin_fmaf(alo, wa, blo * wb), __builtin_fmaf(ahi, wa, bhi * wb));
             }
             *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(o_out) + off) = r;
         }
@@ -133,7 +151,7 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const void* o_a, c
 // where the partials are the tile's pieces (normalised f32 O, natural LSE) and,
 // when accumulating, the (O, LSE) already in o/lse.  One row per D/4 lanes, four
 // elements per lane.
-template <bool F32>
+template <MergeOut T>
 __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restrict__ ws_o,
                                                            const float* __restrict__ ws_lse, void* o, float* lse,
                                                            int first_tile, int n_split, int pieces, int nQt, int H,
@@ -167,55 +185,60 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restri
         for (int p = 0; p < pieces; ++p)
             acc += *reinterpret_cast<const f32x4*>(op + (size_t)p * TR * D) * expf(lp[(size_t)p * TR] - L);
     }
-    if constexpr (F32) {
+    if constexpr (T == MergeOut::F32) {
         *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + c4) = acc;
     } else {
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + c4) =
-            u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            u32x2{pack16<T>(acc[0], acc[1]), pack16<T>(acc[2], acc[3])};
     }
     if (c4 == 0) lse[row] = L;
 }
 
 }  // namespace
 
-hipError_t launch_attn_merge(const MergeArgs& a) {
+template <MergeOut T>
+hipError_t launch_merge_typed(const MergeArgs& a) {
     const int D = (int)a.D;
     const int tpr = D / 8;
     if (tpr > 64) {
         const int64_t blocks = (a.rows + 3) / 4;
-        if (a.f32)
-            hipLaunchKernelGGL(attn_merge_wide_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
-                               a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D);
-        else
-            hipLaunchKernelGGL(attn_merge_wide_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, a.stream,
-                               a.o_a, a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D);
+        hipLaunchKernelGGL(attn_merge_wide_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
+                           a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D);
         return hipGetLastError();
     }
     constexpr int MU = 1;   // row groups per wave (measured best on MI355X)
     const int rpw = 64 / tpr;
     const int64_t waves = (a.rows + (int64_t)rpw * MU - 1) / ((int64_t)rpw * MU);
     const int64_t blocks = (waves + 3) / 4;
-    if (a.f32)
-        hipLaunchKernelGGL((attn_merge_kernel<true, MU>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
-                           a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D, rpw);
-    else
-        hipLaunchKernelGGL((attn_merge_kernel<false, MU>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
-                           a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D, rpw);
+    hipLaunchKernelGGL((attn_merge_kernel<T, MU>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
+                       a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D, rpw);
     return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const MergeArgs& a) {
+    switch (a.o_type) {
+        case MergeOut::F32: return launch_merge_typed<MergeOut::F32>(a);
+        case MergeOut::F16: return launch_merge_typed<MergeOut::F16>(a);
+        default: return launch_merge_typed<MergeOut::BF16>(a);
+    }
+}
+
+template <MergeOut T>
+void launch_pieces_typed(const MergePiecesArgs& a, int64_t blocks) {
+    hipLaunchKernelGGL(merge_pieces_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o, a.ws_lse, a.o,
+                       a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, (int)a.H, a.so, a.Sq, (int)a.D,
+                       a.accumulate ? 1 : 0);
 }
 
 hipError_t launch_merge_pieces(const MergePiecesArgs& a) {
     const int lpr = (int)(a.D / 4);
     const int64_t threads = (int64_t)a.n_split * kAttnTileRows * lpr;
     const int64_t blocks = (threads + 255) / 256;
-    if (a.out_f32)
-        hipLaunchKernelGGL(merge_pieces_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o,
-                           a.ws_lse, a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, (int)a.H, a.so, a.Sq,
-                           (int)a.D, a.accumulate ? 1 : 0);
-    else
-        hipLaunchKernelGGL(merge_pieces_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o,
-                           a.ws_lse, a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, (int)a.H, a.so, a.Sq,
-                           (int)a.D, a.accumulate ? 1 : 0);
+    switch (a.out) {
+        case MergeOut::F32: launch_pieces_typed<MergeOut::F32>(a, blocks); break;
+        case MergeOut::F16: launch_pieces_typed<MergeOut::F16>(a, blocks); break;
+        default: launch_pieces_typed<MergeOut::BF16>(a, blocks); break;
+    }
     return hipGetLastError();
 }
 

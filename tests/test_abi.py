@@ -40,7 +40,8 @@ def header_functions():
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(["cpattn_abi_version", "cpattn_attn_fwd", "cpattn_attn_fwd_ex",
                                          "cpattn_attn_fwd_split_plan", "cpattn_attn_fwd_workspace_size",
-                                         "cpattn_attn_merge", "cpattn_ring_attn_fwd", "cpattn_status_string",
+                                         "cpattn_attn_merge", "cpattn_qk_rmsnorm", "cpattn_ring_attn_fwd",
+                                         "cpattn_status_string",
                                          "cpattn_ulysses_pack", "cpattn_ulysses_unpack"])
 
 
@@ -75,6 +76,10 @@ def test_attn_fwd_validation(L):
     assert fwd(L, k=None) == _lib.E_NULL
     assert fwd(L, i=2) == _lib.E_DTYPE
     assert fwd(L, i=_lib.F32, od=_lib.BF16) == _lib.E_DTYPE
+    assert fwd(L, i=_lib.F16, od=_lib.BF16) == _lib.E_DTYPE           # O in the input type or f32
+    assert fwd(L, i=_lib.BF16, od=_lib.F16) == _lib.E_DTYPE
+    assert fwd(L, i=_lib.F32, od=_lib.F16) == _lib.E_DTYPE
+    assert fwd(L, i=3) == _lib.E_DTYPE
     assert fwd(L, D=96) == _lib.E_HEADDIM
     assert fwd(L, D=256) == _lib.E_HEADDIM
     assert fwd(L, B=0) == _lib.E_SHAPE
@@ -218,6 +223,30 @@ def test_ring_validation(L):
     assert ring(L, scale=0.0) == _lib.E_SCALE
     assert ring(L, lw=E + 16) == _lib.E_ALIAS          # workspace LSE overlaps LSE
     assert ring(L, ow=B_ + 4096) == _lib.E_ALIAS       # workspace O overlaps the K chunks
+
+
+def qkn(L, x=A, w=B_, y=C, rows=100, D=128, eps=1e-6, s=0.3, dt=2):
+    return L.cpattn_qk_rmsnorm(x, w, y, rows, D, eps, s, dt, None)
+
+
+def test_qk_rmsnorm_validation(L):
+    assert qkn(L, x=None) == _lib.E_NULL
+    assert qkn(L, w=None) == _lib.E_NULL
+    assert qkn(L, dt=_lib.F32) == _lib.E_DTYPE
+    assert qkn(L, dt=7) == _lib.E_DTYPE
+    for D in (4, 96, 1024):
+        assert qkn(L, D=D) == _lib.E_HEADDIM
+    assert qkn(L, rows=0) == _lib.E_SHAPE
+    assert qkn(L, rows=1 << 40) == _lib.E_SHAPE
+    assert qkn(L, eps=-1.0) == _lib.E_SCALE
+    assert qkn(L, eps=float("nan")) == _lib.E_SCALE
+    assert qkn(L, s=0.0) == _lib.E_SCALE
+    assert qkn(L, s=float("inf")) == _lib.E_SCALE
+    assert qkn(L, s=1e-30) == _lib.E_SCALE                # rounds to 0 in fp16
+    assert qkn(L, s=1e6) == _lib.E_SCALE                  # overflows fp16
+    assert qkn(L, y=C + 8) == _lib.E_ALIGN
+    assert qkn(L, y=A + 256) == _lib.E_ALIAS              # partial overlap with x
+    assert qkn(L, y=B_ - 16) == _lib.E_ALIAS              # runs into w
 
 
 def rl(L, fn, src=A, dst=B_, B=1, S_l=5520, H=24, D=128, P=8, dt=0, d=0):
