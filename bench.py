@@ -32,16 +32,21 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (256 CUs at 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 LAYERS = 36
-KERNEL_SRC = os.path.join(ROOT, "long_sequence_bidirectional_amd", "csrc", "attn_fwd_bf16.hip")
+KERNEL_SRC = [os.path.join(ROOT, "long_sequence_bidirectional_amd", "csrc", f)
+              for f in ("attn_fwd_kernel.h", "attn_fwd_bf16.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_video_layer_traffic.json")
 # calibration copy for the HBM counters: Ulysses pack of a [44160, 24, 128] bf16 shard
 CALIB_SHAPE = (1, 44160, 24, 128)
 
 
 def kernel_source_hash() -> str:
+    """SHA-256 over the sources of the bf16 attention kernel (template and instantiation)."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(path):
@@ -216,7 +221,7 @@ def main():
                    "B": 1, "H": H, "S": S, "S_text": S_TXT, "D": D, "layers": args.layers},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "attn_fwd_bf16_kernel<128,false> + merge_pieces_kernel<false> "
+                     "kernel": "attn_fwd_mfma_kernel<128,bf16,o bf16,head-major> + merge_pieces_kernel<bf16> "
                                "(self-attention S=44160; the events bracket both)",
                      "avg_launch_ms": round(self_avg, 4), "launches": len(self_ms),
                      "split": split_of(cp, H, S, S, D, ws_self)},
