@@ -49,16 +49,19 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(path):
-    """HBM bytes per self-attention launch from the committed counter summary, or None
-    when the kernel source changed after the counters were taken."""
+def measured_counters(path):
+    """(HBM bytes per self-attention launch, derived counter figures) from the committed
+    counter summary, or (None, None) when the kernel source changed after the counters
+    were taken."""
     if not path or not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    return t.get("traffic_bytes_per_launch")
+        return None, None
+    c = t.get("counters") or {}
+    derived = {k: c[k] for k in ("gfx_clock_ghz", "mfma_busy_frac_at_clock", "busy_cycles_per_mfma") if k in c}
+    return t.get("traffic_bytes_per_launch"), (derived or None)
 
 
 def parse():
@@ -199,7 +202,7 @@ def main():
     self_avg = sum(self_ms) / len(self_ms)
     achieved = flops_self / (self_avg * 1e-3) / 1e12
 
-    traffic = measured_traffic(args.traffic)
+    traffic, counters = measured_counters(args.traffic)
 
     secondary = None if args.no_secondary else secondary_rows(cp, torch, q, k, v, stream)
 
@@ -224,7 +227,8 @@ def main():
                      "kernel": "attn_fwd_mfma_kernel<128,bf16,o bf16,head-major> + merge_pieces_kernel<bf16> "
                                "(self-attention S=44160; the events bracket both)",
                      "avg_launch_ms": round(self_avg, 4), "launches": len(self_ms),
-                     "split": split_of(cp, H, S, S, D, ws_self)},
+                     "split": split_of(cp, H, S, S, D, ws_self),
+                     "counters": counters},
         "wall_s_timed": round(wall, 3),
         "secondary": secondary,
     }
@@ -263,7 +267,30 @@ def profile_pass(cp, torch, q, k, v):
     torch.cuda.synchronize()
     cp.ulysses_pack(shard, 8, cp.SEQ_TO_HEAD, dst=send)
     torch.cuda.synchronize()
-    print(f"profile pass done; calibration copy {shard.numel() * 2} bytes read and written", flush=True)
+    del shard, send
+    # merge and relayout at their per-rank shapes, each over 12 rotating buffer sets (> the 256 MB
+    # MALL), so the counters see HBM traffic: f32 merge of [1,24,5520,128] partials in place, then
+    # pack and unpack of [5520,24,128] bf16 shards
+    from long_sequence_bidirectional_amd import inputs
+    S_L, P, H, D = inputs.S_LOCAL, inputs.CP_DEGREE, inputs.N_HEADS, inputs.HEAD_DIM
+    sets = [(torch.randn((1, H, S_L, D), device="cuda"), torch.randn((1, H, S_L), device="cuda"),
+             torch.randn((1, H, S_L, D), device="cuda"), torch.randn((1, H, S_L), device="cuda")) for _ in range(12)]
+    torch.cuda.synchronize()
+    for oa, la, ob, lb in sets:
+        cp.attn_merge(oa, la, ob, lb, o_out=oa, lse_out=la)
+    torch.cuda.synchronize()
+    del sets
+    shards = [torch.randn((1, S_L, H, D), device="cuda").to(torch.bfloat16) for _ in range(12)]
+    sends = [torch.empty((1, P, S_L, H // P, D), dtype=torch.bfloat16, device="cuda") for _ in range(12)]
+    torch.cuda.synchronize()
+    for a, b in zip(shards, sends):
+        cp.ulysses_pack(a, P, cp.SEQ_TO_HEAD, dst=b)
+    torch.cuda.synchronize()
+    for a, b in zip(shards, sends):
+        cp.ulysses_unpack(b, P, cp.SEQ_TO_HEAD, dst=a.view(1, H // P, S_L * P, D))
+    torch.cuda.synchronize()
+    print(f"profile pass done; calibration copy {CALIB_SHAPE[1] * CALIB_SHAPE[2] * CALIB_SHAPE[3] * 2} bytes "
+          "read and written; 12 cold merges, packs and unpacks", flush=True)
 
 
 def secondary_rows(cp, torch, q, k, v, stream):
