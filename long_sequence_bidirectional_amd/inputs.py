@@ -109,6 +109,38 @@ def small_f32_set(B=1, H=2, S=256, D=64, seed: int = SEED):
     return q, k, v
 
 
+def f32_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to OCP FP8 E4M3 codes (nearest, ties to even; magnitudes above 448
+    saturate to 448).  Returns uint8 codes.  Finite inputs only.
+
+    Works on the float32 bit pattern: normal E4M3 values keep 3 of float32's 23 mantissa bits;
+    below 2^-6 the spacing is fixed at 2^-9, which is handled by rounding x * 2^9 to an
+    integer (exact in float32 for these magnitudes).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    sign = (x.view(np.uint32) >> np.uint32(31)).astype(np.uint8) << np.uint8(7)
+    a = np.minimum(np.abs(x), np.float32(448.0))
+    bits = a.view(np.uint32)
+    # normal range: round the float32 mantissa to 3 bits (ties to even), rebias 127 -> 7
+    lsb = (bits >> np.uint32(20)) & np.uint32(1)
+    r = (bits + np.uint32(0x7FFFF) + lsb) >> np.uint32(20)          # [exp8 | mant3]
+    e = (r >> np.uint32(3)).astype(np.int64) - 127 + 7
+    normal = ((e << 3) | (r & np.uint32(7)).astype(np.int64)).astype(np.int64)
+    # subnormal range (|x| < 2^-6 before rounding): multiples of 2^-9
+    sub = np.rint(a.astype(np.float64) * 512.0).astype(np.int64)       # 0..8 (8 = smallest normal)
+    code = np.where(a < np.float32(2.0 ** -6), sub, normal)
+    return (code.astype(np.uint8) | sign)
+
+
+def normal_e4m3(shape, rng: np.random.Generator, scale: float = 1.0) -> np.ndarray:
+    """N(0, scale^2) draws stored as E4M3 codes (uint8)."""
+    return f32_to_e4m3(normal_f32(shape, rng, scale))
+
+
+def random_e4m3(shape, seed: int, scale: float = 1.0) -> np.ndarray:
+    return normal_e4m3(shape, np.random.Generator(np.random.PCG64(seed)), scale)
+
+
 def normal_f16(shape, rng: np.random.Generator, scale: float = 1.0) -> np.ndarray:
     """N(0, scale^2) draws stored as IEEE fp16 (float32 draws rounded to nearest even)."""
     return normal_f32(shape, rng, scale).astype(np.float16)

@@ -26,6 +26,9 @@ source pages:
   eps 1e-6, weight, cast to fp16, split score scale), with 16-bit rounding at
   the casts the page names ("TensorRT multi-device attention inference in
   practice", step 1).
+* ``e4m3_to_f64`` -- decoding of the 8-bit float inputs of the fp8 attention
+  path; the attention those inputs define is ``attention`` on the decoded
+  values (fp8.py states the reading).
 
 Pins: see tests/test_oracle.py (brute force, closed forms, invariants,
 library special cases, merge algebra, relayout bijections, RMSNorm closed
@@ -35,9 +38,10 @@ from .attention import attention, attention_rows, lse_natural
 from .merge import merge
 from .relayout import ulysses_pack, ulysses_unpack, alltoall, SEQ_TO_HEAD, HEAD_TO_SEQ
 from .qk_norm import rms_norm, qk_prologue, round_to_f16, round_to_bf16
+from .fp8 import e4m3_to_f64
 
 __all__ = [
     "attention", "attention_rows", "lse_natural", "merge",
     "ulysses_pack", "ulysses_unpack", "alltoall", "SEQ_TO_HEAD", "HEAD_TO_SEQ",
-    "rms_norm", "qk_prologue", "round_to_f16", "round_to_bf16",
+    "rms_norm", "qk_prologue", "round_to_f16", "round_to_bf16", "e4m3_to_f64",
 ]

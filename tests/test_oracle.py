@@ -517,3 +517,38 @@ def test_p4_inputs_recipe():
     np.testing.assert_array_equal(inputs._rng(0).standard_normal(4),
                                   np.random.Generator(np.random.PCG64(np.random.SeedSequence(42).spawn(6)[0]))
                                   .standard_normal(4))
+
+
+# ------------------------------------------------------------------ fp8 (E4M3) inputs
+def test_e4m3_decoder_by_hand():
+    codes = np.array([0x00, 0x80, 0x38, 0xB8, 0x08, 0x01, 0x07, 0x7E, 0xFE, 0x3C, 0x40, 0x7F, 0xFF])
+    want = [0.0, -0.0, 1.0, -1.0, 2.0 ** -6, 2.0 ** -9, 7 * 2.0 ** -9, 448.0, -448.0, 1.5, 2.0, np.nan, np.nan]
+    got = oracle.e4m3_to_f64(codes)
+    np.testing.assert_array_equal(got[:11], want[:11])
+    assert np.isnan(got[11]) and np.isnan(got[12])
+    # every finite code decodes to a distinct value, symmetric in sign, ordered by code within a sign
+    finite = [c for c in range(128) if c != 0x7F]
+    v = oracle.e4m3_to_f64(np.array(finite))
+    assert np.all(np.diff(v) > 0) and len(set(v)) == len(v)
+    np.testing.assert_array_equal(oracle.e4m3_to_f64(np.array(finite) | 0x80), -v)
+
+
+def test_e4m3_encoder_is_nearest_even():
+    """The input recipe's encoder against brute force over all finite codes: the nearest value,
+    ties to the even code, saturation at 448."""
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    vals = oracle.e4m3_to_f64(finite)
+    g = np.random.Generator(np.random.PCG64(910))
+    x = np.concatenate([g.standard_normal(4000) * s for s in (0.01, 1.0, 30.0, 300.0)]).astype(np.float32)
+    # exact ties: midpoints between neighbouring positive values
+    pos = np.sort(vals[vals > 0])
+    x = np.concatenate([x, ((pos[:-1] + pos[1:]) / 2).astype(np.float32), np.float32([1000.0, -1000.0, 0.0])])
+    codes = inputs.f32_to_e4m3(x)
+    got = oracle.e4m3_to_f64(codes)
+    for xi, gi, ci in zip(x.astype(np.float64), got, codes):
+        xs = float(np.clip(xi, -448.0, 448.0))
+        d = np.abs(vals - xs)
+        best = np.flatnonzero(d == d.min())
+        if len(best) > 1:                        # a tie: the code with an even mantissa
+            best = [b for b in best if finite[b] % 2 == 0]
+        assert gi == vals[best[0]] or (gi == 0.0 and vals[best[0]] == 0.0), (xi, gi, ci)
