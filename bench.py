@@ -380,7 +380,35 @@ def secondary_rows(cp, torch, q, k, v, stream):
     out["unpack_s2h_GBps"] = round(nbytes / ms / 1e6, 1)
     out.update(cold_rows(cp, torch, stream))
     out.update(p4_rows(cp, torch, stream))
+    out.update(fp8_rows(cp, torch, stream))
     return out
+
+
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 matrix-core peak (twice bf16)
+
+
+def fp8_rows(cp, torch, stream, iters=10):
+    """Self-attention S=44160, H=24, D=128 with E4M3 inputs (N(0,1) draws rounded to E4M3,
+    scales 1) on the fp8 matrix cores; O in bf16."""
+    import numpy as np
+    from long_sequence_bidirectional_amd import inputs
+    S, H, D = inputs.S_VIDEO, inputs.N_HEADS, inputs.HEAD_DIM
+    q8, k8, v8 = (torch.from_numpy(inputs.random_e4m3((1, H, S, D), 7300 + i)).cuda() for i in range(3))
+    o = torch.empty((1, H, S, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, H, S), dtype=torch.float32, device="cuda")
+    fn = lambda: cp.attn_fwd_fp8(q8, k8, v8, o=o, lse=lse, stream=stream)
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(iters):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    tf = 4.0 * H * S * S * D / ms / 1e9
+    return {"fp8_self_ms": round(ms, 3), "fp8_self_tflops": round(tf, 1),
+            "fp8_self_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
 
 
 def p4_rows(cp, torch, stream, iters=50):

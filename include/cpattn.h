@@ -30,6 +30,9 @@
  *    into the running (O, LSE) by the attn_merge rule (first page, "Ring
  *    Attention").
  *
+ *  - attn_fwd_fp8: the same attention with 8-bit float (E4M3) inputs on the
+ *    fp8 matrix cores.
+ *
  *  - qk_rmsnorm: the QK-RMSNorm prologue (fp32 RMSNorm over head_dim, cast
  *    to the 16-bit type, split score scale) of the attention sample in
  *    "TensorRT multi-device attention inference in practice", step 1.
@@ -171,6 +174,28 @@ cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, vo
                                  float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
                                  uint32_t flags, void* workspace, uint64_t workspace_bytes,
                                  hipStream_t stream);
+
+/*
+ * Attention with 8-bit float inputs (OCP FP8 E4M3), one f32 scale per tensor.
+ *
+ *   q [B, H, Sq, D], k and v [B, H, Skv, D]  E4M3 bytes (real value = decoded byte * scale)
+ *   o [B, H, Sq, D]  o_dtype = BF16 or F32 (else CPATTN_E_DTYPE)   lse [B, H, Sq] f32
+ *   (with CPATTN_FLAG_SEQ_MAJOR: q, o [B, Sq, H, D], k, v [B, Skv, H, D]; lse unchanged)
+ *
+ * The result is attention (as cpattn_attn_fwd defines it, with `scale` on the scores) of
+ * the real-valued tensors q * q_scale, k * k_scale, v * v_scale.  The pages name
+ * quantisation as an inference optimisation ("Scaling AI inference across multiple GPUs
+ * using NVIDIA TensorRT with multi-device inference support", opening section) but give
+ * no recipe; this one runs both products on gfx950's fp8 matrix cores (twice the bf16
+ * rate) with f32 scores and softmax state, and rounds the softmax weights to E4M3 (as
+ * p * 2^7, p <= 2) for the PV product.  D = 128 only (CPATTN_E_HEADDIM); scales finite
+ * and > 0 (CPATTN_E_SCALE); flags: 0 or CPATTN_FLAG_SEQ_MAJOR (else CPATTN_E_FLAGS);
+ * Skv = 0 gives O = 0, LSE = -inf.  Other checks as for cpattn_attn_fwd.
+ */
+cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
+                                  float q_scale, float k_scale, float v_scale, cpattn_dtype o_dtype,
+                                  uint32_t flags, hipStream_t stream);
 
 /*
  * Workspace bytes cpattn_attn_fwd_ex uses for this problem on the CURRENT

@@ -11,6 +11,7 @@ torch provides device memory and streams.
   attn_fwd_split_plan(B, H, Sq, Skv, D, slots, ws_bytes)  -> (split_tiles, pieces, bytes)
   attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None) -> (o_out, lse_out)
   ring_attn_fwd(q, k_chunks, v_chunks, ...)               -> (o, lse)
+  attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, ...) -> (o, lse)
   qk_rmsnorm(x, w, eps=1e-6, post_scale=1.0, out=None)   -> out
   ulysses_pack(src, P, direction, dst=None)               -> dst
   ulysses_unpack(src, P, direction, dst=None)             -> dst
@@ -24,7 +25,7 @@ from ._lib import (BF16, F16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ,
                    lib)
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge",
-           "qk_rmsnorm", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
+           "qk_rmsnorm", "attn_fwd_fp8", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
            "SEQ_TO_HEAD", "HEAD_TO_SEQ", "CpattnError", "lib"]
 
 
@@ -107,6 +108,40 @@ def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, out_dtype=None, workspace
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     flags = (FLAG_ACCUMULATE if accumulate else 0) | (FLAG_SEQ_MAJOR if seq_major else 0)
     check("cpattn_attn_fwd_ex", lib().cpattn_attn_fwd_ex(*args, flags, ws_ptr, ws_bytes, _stream(stream)))
+    return o, lse
+
+
+def attn_fwd_fp8(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, o=None, lse=None, scale=None,
+                 out_dtype=None, seq_major=False, stream=None):
+    """Attention of E4M3 inputs (uint8 codes or torch.float8_e4m3fn) with per-tensor scales;
+    O in bf16 (default) or f32.  Shapes as attn_fwd_ex (head- or sequence-major), D = 128."""
+    torch = _torch()
+    for t in (q, k, v):
+        if t.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+            raise TypeError("fp8 attention takes E4M3 codes (uint8 or float8_e4m3fn)")
+    if seq_major:
+        B, Sq, H, D = q.shape
+        Skv = k.shape[1]
+        kv_shape, o_shape = (B, Skv, H, D), (B, Sq, H, D)
+    else:
+        B, H, Sq, D = q.shape
+        Skv = k.shape[2]
+        kv_shape, o_shape = (B, H, Skv, D), (B, H, Sq, D)
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o is None:
+        o = torch.empty(o_shape, dtype=out_dtype or torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if tuple(o.shape) != o_shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
+        raise ValueError(f"o must be {o_shape} and lse float32 [B,H,Sq]")
+    flags = FLAG_SEQ_MAJOR if seq_major else 0
+    st = lib().cpattn_attn_fwd_fp8(_dev(q, "q"), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
+                                   _dev(o, "o"), _dev(lse, "lse"), B, H, Sq, Skv, D, float(scale), float(q_scale),
+                                   float(k_scale), float(v_scale), _dtype_code(o), flags, _stream(stream))
+    check("cpattn_attn_fwd_fp8", st)
     return o, lse
 
 

@@ -30,6 +30,7 @@ _PI64, _PU64 = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64)
 SIGNATURES = [
     ("cpattn_attn_fwd", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _P]),
     ("cpattn_attn_fwd_ex", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _U32, _P, _U64, _P]),
+    ("cpattn_attn_fwd_fp8", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _F, _F, _F, _E, _U32, _P]),
     ("cpattn_attn_fwd_workspace_size", _E, [_I64, _I64, _I64, _I64, _I64, _E, _E, _PU64]),
     ("cpattn_attn_fwd_split_plan", _E, [_I64, _I64, _I64, _I64, _I64, _I64, _U64, _PI64, _PI64, _PU64]),
     ("cpattn_attn_merge", _E, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _E, _P]),

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libcpattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_fwd_f32.hip", "merge.hip", "relayout.hip",
+SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_fwd_f32.hip", "attn_fwd_fp8.hip", "merge.hip", "relayout.hip",
            "qk_norm.hip"]
 
 FLAGS = [

@@ -278,6 +278,52 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, con
                     ws_pieces, stream);
 }
 
+CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                                                int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                                float scale, float q_scale, float k_scale, float v_scale,
+                                                cpattn_dtype o_dtype, uint32_t flags, hipStream_t stream) {
+    if ((flags & ~(uint32_t)CPATTN_FLAG_SEQ_MAJOR) != 0) return CPATTN_E_FLAGS;
+    const bool seq_major = (flags & CPATTN_FLAG_SEQ_MAJOR) != 0;
+    if (!q || !o || !lse || (Skv != 0 && (!k || !v))) return CPATTN_E_NULL;
+    if (o_dtype != CPATTN_BF16 && o_dtype != CPATTN_F32) return CPATTN_E_DTYPE;
+    AttnCheck c;
+    cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, scale, 32, &c);
+    if (st != CPATTN_OK) return st;
+    if (D != 128) return CPATTN_E_HEADDIM;
+    for (float s : {q_scale, k_scale, v_scale})
+        if (!(s > 0.f) || !isfinite(s)) return CPATTN_E_SCALE;
+    if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || (Skv && (!aligned16(k) || !aligned16(v))))
+        return CPATTN_E_ALIGN;
+    const int64_t osz = dtype_size(o_dtype);
+    const Range rq = range(q, c.q_elems), rk = range(k, c.kv_elems), rv = range(v, c.kv_elems);
+    const Range ro = range(o, c.q_elems * osz), rl = range(lse, c.rows * 4);
+    if (overlap(ro, rl) || overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) ||
+        overlap(rl, rk) || overlap(rl, rv))
+        return CPATTN_E_ALIAS;
+    if (Skv == 0) return hip_status(cpattn::launch_fill_empty(o, c.q_elems * osz, lse, c.rows, stream));
+    cpattn::AttnFp8Args a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.BH = B * H;
+    a.H = H;
+    a.Sq = Sq;
+    a.Skv = Skv;
+    a.seq_major = seq_major;
+    a.sq = layout_strides(H, Sq, D, seq_major);
+    a.skv = layout_strides(H, Skv, D, seq_major);
+    a.so = a.sq;
+    a.scale = scale;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.out_f32 = o_dtype == CPATTN_F32;
+    a.stream = stream;
+    return hip_status(cpattn::launch_attn_fwd_fp8(a));
+}
+
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd_split_plan(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                                                        int64_t slots, uint64_t workspace_bytes,
                                                        int64_t* split_tiles, int64_t* pieces,

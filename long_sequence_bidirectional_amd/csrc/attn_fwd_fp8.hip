@@ -1,0 +1,318 @@
+// Non-causal attention forward with 8-bit float inputs (OCP FP8 E4M3) on gfx950's
+// v_mfma_f32_32x32x64_f8f6f4 (twice the bf16 matrix-core rate).
+//
+// Same method as the bf16 kernel (blockwise online softmax, "Scaling AI inference
+// across multiple GPUs using NVIDIA TensorRT with multi-device inference support",
+// section "Ring Attention"; low-precision inference named in its opening section):
+// Q, K, V arrive as E4M3 bytes with one f32 scale per tensor, scores and softmax
+// state are f32, the softmax weights are rounded to E4M3 for the PV product, and O
+// is stored as bf16 or f32.  D = 128.
+//
+// Work split and schedule are those of the bf16 kernel: 8 waves, 256 query rows per
+// workgroup, waves w and w+4 on one SIMD alternating an MFMA slot (4 QK + 4 PV MFMAs
+// per 64-key block) with a softmax slot, K/V through three LDS buffers by direct
+// global->LDS loads, Q^T in registers.
+//
+// Operand layouts of the 32x32x64 fp8 MFMA: lane (row/column l%32, half h = l/32)
+// holds 32 bytes of its row of A (column of B); byte j of half h of A meets byte j
+// of half h of B.  QK: both operands hold d = 64*ks + 32*h + j.  PV: the B operand
+// is P^T straight from the S^T accumulator, whose lane (query, h) holds accumulator
+// rows (i/4)*8 + 4h + i%4 of each 32-key tile.  K rows are stored in LDS with bits 2
+// and 3 of the row index swapped, so that accumulator row rho holds the key
+// rho ^ swap23, and half h's bytes 8c..8c+7 are the 8 consecutive keys 16c + 8h + e.
+// The V^T A operand then comes from four ds_read_b64_tr_b8 per MFMA: in each 16-lane
+// group, lane pair (2i, 2i+1) addresses row r0 + i (bytes 0-7 and 8-15 of a 16-byte
+// column block) and lane L receives column L of the 8 rows.
+//
+// Rows are 128 bytes; 16-byte chunks are XOR-swizzled by (row >> 1) & 7 so that both
+// the K reads (16 rows x one chunk) and the transposing V reads (8 rows x one chunk)
+// hit distinct banks.
+//
+// Softmax: t = s * c with c = scale * log2(e) * q_scale * k_scale; the running max is
+// raised only when a block's max exceeds it by more than 1, so p = exp2(t - m) <= 2;
+// the weights enter the PV product as E4M3 of p * 2^7 (<= 256 < 448, and typical
+// weights stay in E4M3's normal range), O = sum(p8 v) * v_scale / (2^7 * l) with the
+// row sum l of the unrounded f32 weights, LSE = (m + log2 l) * ln 2.
+#include <utility>
+
+#include "common.h"
+#include "kernels.h"
+
+#define CPATTN_AI __attribute__((always_inline))
+
+namespace cpattn {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+#define GLOBAL_PTR(T, p) ((const __attribute__((address_space(1))) T*)(p))
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+constexpr int kD = 128;
+constexpr int kBM = kAttnTileRows;   // 256 query rows per workgroup
+constexpr int kBN = 64;              // keys per block
+constexpr int kNBUF = 3;
+constexpr float kRaiseTh = 1.0f;     // raise m only when a block max exceeds it by more than 1
+constexpr float kPScale = 128.0f;    // p enters the PV product as E4M3(p * 2^7)
+
+// stored 16-byte chunk of logical chunk c of row r
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// LDS row of K that holds key (row) r of the block, and back: swap bits 2 and 3
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// two f32 -> two E4M3 bytes in the low (HI=false) or high half of `old`, nearest even
+template <bool HI>
+__device__ __forceinline__ int pack_fp8x2(float a, float b, int old) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+template <bool OUT_F32, bool SEQ>
+__global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+                                                           const uint8_t* __restrict__ v, void* __restrict__ o,
+                                                           float* __restrict__ lse, int Sq, int Skv, int nQt, int H,
+                                                           Strides sq, Strides skv, Strides so, int total,
+                                                           int per_xcd, float c, float out_scale) {
+    constexpr int D = kD, BN = kBN;
+    constexpr int NKS = D / 64;            // k-steps of QK (64 d each)
+    constexpr int NDT = D / 32;            // 32-wide d tiles of O^T
+    constexpr int NKT = BN / 32;           // 32-key tiles of S^T
+    constexpr int RPP = 1024 / D;          // rows per 1 KB load piece (8)
+
+    __shared__ __attribute__((aligned(1024))) uint8_t Ks[kNBUF][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint8_t Vs[kNBUF][BN * D];
+
+    const int bid = blockIdx.x;
+    const int logical = (bid % kNumXcd) * per_xcd + bid / kNumXcd;
+    if (logical >= total) return;
+    const int bh = logical / nQt;
+    const int qt = logical - bh * nQt;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int L16 = lane & 15;
+    const int g16 = (lane >> 4) & 1;
+    const int group = wave >> 2;
+
+    const int64_t q_row = SEQ ? sq.row : D, kv_row = SEQ ? skv.row : D, o_row = SEQ ? so.row : D;
+    const int b = SEQ ? bh / H : 0, h = SEQ ? bh - b * H : 0;
+    const uint8_t* qp = q + (SEQ ? b * sq.batch + h * sq.head : (int64_t)bh * Sq * D);
+    const uint8_t* kp = k + (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv * D);
+    const uint8_t* vp = v + (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv * D);
+    const int64_t o_base = SEQ ? b * so.batch + h * so.head : (int64_t)bh * Sq * D;
+    const int qrow = qt * kBM + wave * 32 + l32;
+    const int nblk = (Skv + BN - 1) / BN;
+
+    // one 1 KB piece per wave per tensor: rows 8*wave .. 8*wave+7 of the block
+    auto load_block = [&](const uint8_t* src, uint8_t* dst, int j, bool is_k) CPATTN_AI {
+        const int row = wave * RPP + lane / 8;                       // LDS row
+        const int key = is_k ? swap23(row) : row;                    // key stored there
+        const int ch = (lane % 8) ^ swz8(row);                       // logical chunk of this lane
+        const int r = min(j * BN + key, Skv - 1);
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src + r * kv_row + ch * 16),
+                                         LDS_PTR(void, dst + wave * 1024), 16, 0, 0);
+    };
+
+    // Q^T operand: lane (query l32, half hh), k-step ks: bytes d = 64 ks + 32 hh .. +31
+    i32x8 qreg[NKS];
+    {
+        const uint8_t* qr = qp + min(qrow, Sq - 1) * q_row + 32 * hh;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(qr + 64 * ks);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(qr + 64 * ks + 16);
+            qreg[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                             (int)hi[3]};
+        }
+    }
+    // K operand of tile kt, k-step ks: LDS row 32 kt + l32, logical chunks 4 ks + 2 hh, +1
+    auto read_k = [&]<int BUF>(ic<BUF>, int kt, int ks) CPATTN_AI -> i32x8 {
+        const int row = kt * 32 + l32;
+        const uint8_t* base = &Ks[BUF][row * D];
+        const int c0 = 4 * ks + 2 * hh;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + ((c0 ^ swz8(row)) * 16));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + (((c0 + 1) ^ swz8(row)) * 16));
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    // V^T operand of d tile dt: four transposing reads, rows 16 c + 8 hh + (L16 / 2), chunk of
+    // columns dt*32 + 16 g16 .. +15, bytes 8 (L16 % 2) of it
+    auto read_vt = [&]<int BUF>(ic<BUF>, int dt) CPATTN_AI -> i32x8 {
+        i32x2 r[4];
+        const int lchunk = dt * 2 + g16;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const int row = 16 * cc + 8 * hh + (L16 >> 1);
+            r[cc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                LDS_PTR(i32x2, &Vs[BUF][row * D + ((lchunk ^ swz8(row)) * 16) + 8 * (L16 & 1)]));
+        }
+        return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+    };
+
+    f32x16 oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+    f32x16 s[NKT];
+    i32x8 pb;                  // P^T bytes: j = 16 kt + i
+    float m_run = -INFINITY, l_run = 0.f, alpha = 1.f;
+
+    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1)
+    auto M = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        constexpr int KB = R, VB = (R + 2) % 3;
+        __builtin_amdgcn_s_setprio(1);
+        if (j < nblk) {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma8(read_k(ic<KB>{}, kt, ks), qreg[ks], s[kt]);
+        }
+        if (j >= 1) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma8(read_vt(ic<VB>{}, dt), pb, oacc[dt]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // SM_j: softmax of S_j -> P_j (E4M3 of p * 2^7), row statistics, O *= alpha when raised
+    auto SM = [&](int j) CPATTN_AI {
+        if (j == nblk - 1 && (Skv % BN) != 0) {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = j * BN + swap23(kt * 32 + (i >> 2) * 8 + hh * 4 + (i & 3));
+                    if (key >= Skv) s[kt][i] = -INFINITY;
+                }
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+        mx = max_across_halves(mx) * c;
+        const bool raise = mx > m_run + kRaiseTh;
+        const float m_new = raise ? mx : m_run;
+        alpha = exp2_fast(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                float p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p[e] = exp2_fast(__builtin_fmaf(s[kt][w * 4 + e], c, -m_new));
+                    psum += p[e];
+                }
+                int word = pack_fp8x2<false>(p[0] * kPScale, p[1] * kPScale, 0);
+                word = pack_fp8x2<true>(p[2] * kPScale, p[3] * kPScale, word);
+                pb[kt * 4 + w] = word;
+            }
+        l_run = l_run * alpha + psum;
+        asm volatile("" : "+v"(l_run));
+        asm volatile("" : "+v"(pb));
+        if (__ballot(raise) != 0) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        }
+    };
+    auto issue = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        if (j + 2 < nblk) load_block(kp, Ks[(R + 2) % 3], j + 2, true);
+        if (j + 1 < nblk) load_block(vp, Vs[(R + 1) % 3], j + 1, false);
+    };
+    // wait until at most this wave's latest issue (two loads when full) is in flight
+    auto wait_older = [&](int jl) CPATTN_AI {
+        if (jl + 2 < nblk) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    load_block(kp, Ks[0], 0, true);
+    if (nblk > 1) load_block(kp, Ks[1], 1, true);
+    load_block(vp, Vs[0], 0, false);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    auto slot_barrier = [&]() CPATTN_AI { asm volatile("s_barrier" ::: "memory"); };
+    auto body = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        M(ic<R>{}, j);
+        __builtin_amdgcn_sched_barrier(0);
+        slot_barrier();
+        if (group != 0) issue(ic<(R + 1) % 3>{}, j + 1);
+        else issue(ic<R>{}, j);
+        if (j < nblk) SM(j);
+        wait_older(group != 0 ? j + 1 : j);
+        __builtin_amdgcn_sched_barrier(0);
+        slot_barrier();
+    };
+    if (group != 0) {
+        issue(ic<0>{}, 0);
+        slot_barrier();
+    }
+    int j = 0;
+    for (; j + 2 <= nblk; j += 3) {
+        body(ic<0>{}, j);
+        body(ic<1>{}, j + 1);
+        body(ic<2>{}, j + 2);
+    }
+    if (j <= nblk) body(ic<0>{}, j);
+    if (j + 1 <= nblk) body(ic<1>{}, j + 1);
+    if (group == 0) slot_barrier();
+
+    const float l_tot = sum_across_halves(l_run);
+    if (qrow < Sq) {
+        const float inv = l_tot > 0.f ? out_scale / l_tot : 0.f;     // v_scale / (2^7 l)
+        const int64_t orow = o_base + qrow * o_row;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + g * 8 + hh * 4;
+                const float x0 = oacc[dt][g * 4 + 0] * inv, x1 = oacc[dt][g * 4 + 1] * inv;
+                const float x2 = oacc[dt][g * 4 + 2] * inv, x3 = oacc[dt][g * 4 + 3] * inv;
+                if constexpr (OUT_F32)
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = f32x4{x0, x1, x2, x3};
+                else
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + d0) =
+                        u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+            }
+        if (hh == 0) lse[(int64_t)bh * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+template <bool OUT_F32, bool SEQ>
+hipError_t launch_fp8_typed(const AttnFp8Args& a) {
+    const int nQt = (int)((a.Sq + kBM - 1) / kBM);
+    const int64_t total = a.BH * nQt;
+    const int per_xcd = (int)((total + kNumXcd - 1) / kNumXcd);
+    const float c = (float)((double)a.scale * 1.4426950408889634 * (double)a.q_scale * (double)a.k_scale);
+    const float out_scale = (float)((double)a.v_scale / (double)kPScale);
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32, SEQ>), dim3(per_xcd * kNumXcd), dim3(512), 0, a.stream,
+                       static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+                       static_cast<const uint8_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)a.H, a.sq,
+                       a.skv, a.so, (int)total, per_xcd, c, out_scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_fp8(const AttnFp8Args& a) {
+    if (a.seq_major) return a.out_f32 ? launch_fp8_typed<true, true>(a) : launch_fp8_typed<false, true>(a);
+    return a.out_f32 ? launch_fp8_typed<true, false>(a) : launch_fp8_typed<false, false>(a);
+}
+
+}  // namespace cpattn

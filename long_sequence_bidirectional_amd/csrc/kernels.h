@@ -57,6 +57,23 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f16(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a);
 
+// Attention with OCP FP8 E4M3 inputs (D = 128), one f32 scale per tensor.
+struct AttnFp8Args {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int64_t BH, H, Sq, Skv;
+    bool seq_major;
+    Strides sq, skv, so;
+    float scale, q_scale, k_scale, v_scale;
+    bool out_f32;            // O in f32 (else bf16)
+    hipStream_t stream;
+};
+
+hipError_t launch_attn_fwd_fp8(const AttnFp8Args& a);
+
 // Resident workgroups per CU of the bf16 attention kernel (0 if the runtime cannot tell).
 int attn_fwd_bf16_blocks_per_cu(int64_t D, bool out_f32);
 

@@ -34,11 +34,12 @@ def L():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(cpattn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(cpattn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(["cpattn_abi_version", "cpattn_attn_fwd", "cpattn_attn_fwd_ex",
+                                         "cpattn_attn_fwd_fp8",
                                          "cpattn_attn_fwd_split_plan", "cpattn_attn_fwd_workspace_size",
                                          "cpattn_attn_merge", "cpattn_qk_rmsnorm", "cpattn_ring_attn_fwd",
                                          "cpattn_status_string",
@@ -223,6 +224,28 @@ def test_ring_validation(L):
     assert ring(L, scale=0.0) == _lib.E_SCALE
     assert ring(L, lw=E + 16) == _lib.E_ALIAS          # workspace LSE overlaps LSE
     assert ring(L, ow=B_ + 4096) == _lib.E_ALIAS       # workspace O overlaps the K chunks
+
+
+def fp8(L, q=A, k=B_, v=C, o=D_, lse=E, B=1, H=2, Sq=256, Skv=256, D=128, scale=0.1, qs=1.0, ks=1.0, vs=1.0,
+        od=0, flags=0):
+    return L.cpattn_attn_fwd_fp8(q, k, v, o, lse, B, H, Sq, Skv, D, scale, qs, ks, vs, od, flags, None)
+
+
+def test_attn_fwd_fp8_validation(L):
+    assert fp8(L, q=None) == _lib.E_NULL
+    assert fp8(L, k=None) == _lib.E_NULL
+    assert fp8(L, od=_lib.F16) == _lib.E_DTYPE
+    assert fp8(L, D=64) == _lib.E_HEADDIM
+    assert fp8(L, D=96) == _lib.E_HEADDIM
+    assert fp8(L, Sq=0) == _lib.E_SHAPE
+    assert fp8(L, scale=0.0) == _lib.E_SCALE
+    assert fp8(L, qs=0.0) == _lib.E_SCALE
+    assert fp8(L, vs=float("inf")) == _lib.E_SCALE
+    assert fp8(L, flags=_lib.FLAG_ACCUMULATE) == _lib.E_FLAGS
+    assert fp8(L, flags=4) == _lib.E_FLAGS
+    assert fp8(L, o=E + 16) == _lib.E_ALIGN or fp8(L, o=E + 16) == _lib.E_ALIAS
+    assert fp8(L, o=A + 1024) == _lib.E_ALIAS          # o on top of q
+    assert fp8(L, lse=C + 64) == _lib.E_ALIAS          # lse on top of v
 
 
 def qkn(L, x=A, w=B_, y=C, rows=100, D=128, eps=1e-6, s=0.3, dt=2):
