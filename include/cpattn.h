@@ -167,7 +167,8 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
  * read as [S, H, D] (first page, "DeepSpeed Ulysses"): attention reads that
  * buffer in place and writes o straight into the send buffer of the second
  * all-to-all, so no relayout pass is needed on the head side.  Same results
- * as the head-major call on the transposed tensors, bit for bit.
+ * as the head-major call on the transposed tensors, bit for bit.  A token
+ * row (H * D elements) must be shorter than 2^25 elements (CPATTN_E_SHAPE).
  */
 cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,

@@ -259,6 +259,8 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, con
     const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, &ck);
     if (st != CPATTN_OK) return st;
     if (acc && (!dtype_16bit(in_dtype) || o_dtype != CPATTN_F32)) return CPATTN_E_DTYPE;
+    // the 16-bit kernels address a 64-row K/V block with 32-bit byte offsets
+    if (seq_major && H * D >= (int64_t(1) << 25)) return CPATTN_E_SHAPE;
     if (workspace_bytes != 0 && !workspace) return CPATTN_E_NULL;
     int64_t ws_pieces = 0;
     float *ws_o = nullptr, *ws_lse = nullptr;

@@ -28,26 +28,38 @@
 //   i.e. keys 16t + 8*(j/4) + 4h + j%4.
 //
 // Registers and LDS.  Each wave keeps its Q^T operand (32 rows x D) in
-// registers for the whole tile.  K and V blocks (three buffers each) are stored
-// in LDS row-major with 16-byte chunks XOR-swizzled per row and filled by direct
-// global->LDS loads (global_load_lds_dwordx4: lane i writes bytes 16i..16i+15
-// of a 1 KB piece, so a wave's load is a plain copy and needs no registers).
-// The V^T A-operand of the PV product comes from two ds_read_b64_tr_b16 per
-// MFMA: in each 16-lane group, lane L points at row kv0 + L/4, columns
-// d0 + 4(L%4) .. +3 and receives V[kv0 .. kv0+3][d0 + L], i.e. four keys of
-// one head-dim column -- exactly the per-lane k-slots above.  The swizzles
-// make the K reads (16 rows x one chunk) and the V transposing reads
-// (4 rows x 4 chunks) hit 64 distinct banks.
+// registers for the whole tile.  K and V blocks (four buffers each, 128 KB) are
+// stored in LDS row-major with 16-byte chunks XOR-swizzled per row and filled by
+// direct global->LDS loads (global_load_lds_dwordx4: lane i writes bytes
+// 16i..16i+15 of a 1 KB piece, so a wave's load is a plain copy and needs no
+// registers).  A load is the block's wave-uniform base (SGPRs) plus a per-lane
+// byte offset that is the same for every full block, so no address arithmetic
+// runs per block and no register that a load in flight still has to read is
+// rewritten.  The V^T A-operand of the PV product comes from two
+// ds_read_b64_tr_b16 per MFMA: in each 16-lane group, lane L points at row
+// kv0 + L/4, columns d0 + 4(L%4) .. +3 and receives V[kv0 .. kv0+3][d0 + L],
+// i.e. four keys of one head-dim column -- exactly the per-lane k-slots above.
+// The swizzles make the K reads (16 rows x one chunk) and the V transposing
+// reads (4 rows x 4 chunks) hit 64 distinct banks.
 //
 // Schedule.  Per key block j a wave runs an MFMA slot M_j = {S_j = K_j Q^T,
 // O += V_{j-1} P_{j-1}} and a softmax slot SM_j (max, exp2, row sum, bf16
 // weights, rescale of O when needed).  Waves w and w+4 share a SIMD; group 1
 // (waves 4-7) runs one slot behind group 0, so on every SIMD one wave issues
 // MFMAs while the other computes exponentials, with one workgroup barrier
-// per slot.  In an MFMA slot the operand reads run three MFMAs ahead.  Global
-// loads are issued from softmax slots, two slots before their data is needed
-// (three K/V buffers), and the slot barriers are plain s_barrier: each wave
-// waits only for its own older loads (vmcnt) before arriving.
+// per slot.  Two measured limits shape the slots:
+//  - a wave's LDS reads return at about 32 bytes per clock, so the MFMA slot
+//    (1 KB of operands per MFMA) cannot hide all of them behind its MFMAs.
+//    The softmax slot therefore reads the first 8 K fragments of the wave's
+//    next MFMA slot into registers, and the MFMA slot reads the rest four
+//    MFMAs ahead;
+//  - a CU's vector-memory path accepts one 1 KB global->LDS load per ~32
+//    clocks and a wave stalls at issue until its loads are taken.  A softmax
+//    slot that issued loads would stall on the critical path, so each wave
+//    issues its four pieces inside its MFMA slot, spread between MFMAs, three
+//    blocks ahead of use (four buffers).
+// Slot barriers are plain s_barrier: each wave waits only for its own older
+// loads (vmcnt) before arriving.
 //
 // Softmax in base 2: t = s * scale * log2(e), p = exp2(t - m), natural
 // LSE = (m + log2 l) * ln 2.  The running max m is only raised when a block's
@@ -76,8 +88,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = kAttnTileRows;    // query rows per workgroup (8 waves x 32)
 constexpr int kBN = 64;               // keys per block
-constexpr int kReadAhead = 3;         // MFMA operand reads issued this many MFMAs ahead
-constexpr int NBUF = 3;               // K and V buffers in LDS
+constexpr int kReadAhead = 4;         // MFMA operand reads issued this many MFMAs ahead
+constexpr int NBUF = 4;               // K and V buffers in LDS
 constexpr float kRescaleTh = 8.0f;    // raise m only when the block max exceeds it by > 2^8
 
 template <int I>
@@ -166,6 +178,7 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
@@ -184,17 +197,43 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     const uint16_t* vp = v + kv_off;
     const int qrow = qt * kBM + wave * 32 + l32;
 
-    // ---- direct global -> LDS loads of K/V blocks (rows clamped to the last valid one)
-    auto load_block = [&](const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
-        uint16_t* base = dst + wave * LOADS_PER_WAVE * 512;
-        auto one = [&]<int I>(ic<I>) CPATTN_AI {
-            const int row = (wave * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
+    // ---- direct global -> LDS loads of K/V blocks.  Each wave moves its LOADS_PER_WAVE 1 KB
+    // pieces of a block; the per-lane byte offsets within a full block are constant, so a load
+    // is the block's (wave-uniform) base in SGPRs plus a fixed VGPR offset and no address
+    // arithmetic runs per block.  The last, partial block clamps rows to the last valid one.
+    uint32_t koffb[LOADS_PER_WAVE], voffb[LOADS_PER_WAVE];
+#pragma unroll
+    for (int I = 0; I < LOADS_PER_WAVE; ++I) {
+        const int row = (wave_u * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
+        koffb[I] = (uint32_t)((row * kv_row + (((lane % NC) ^ swz_k<D>(row)) * 8)) * 2);
+        voffb[I] = (uint32_t)((row * kv_row + (((lane % NC) ^ swz_v<D>(row)) * 8)) * 2);
+    }
+    // One 1 KB piece: global address sb + off + I*1024 -> LDS lds + I*1024 + 16*lane.  M0 holds
+    // the LDS base; nothing else in this kernel uses M0 (no LDS DMA builtins, no indexed
+    // register access), so the asm sets it itself.
+    auto dma = [&]<int I>(ic<I>, uint32_t off, const char* blk, uint32_t lds) CPATTN_AI {
+        const char* sb = blk - I * 1024;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
+                     :: "v"(off), "s"(sb), "s"(lds), "n"(I * 1024) : "memory", "m0");
+#pragma clang diagnostic pop
+    };
+    auto load_piece = [&]<int I>(ic<I>, const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
+        const uint32_t lds = (uint32_t)(uintptr_t)LDS_PTR(void, dst + wave_u * LOADS_PER_WAVE * 512);
+        const char* blk = reinterpret_cast<const char*>(src + (int64_t)j * BN * kv_row);
+        if ((j + 1) * BN <= Skv) {
+            if (is_v) dma(ic<I>{}, voffb[I], blk, lds);
+            else dma(ic<I>{}, koffb[I], blk, lds);
+        } else {
+            const int row = (wave_u * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
             const int ch = (lane % NC) ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
-            const int r = min(j * BN + row, Skv - 1);
-            const char* g = reinterpret_cast<const char*>(src + r * kv_row + ch * 8) - I * 1024;
-            __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, g), LDS_PTR(void, base), 16, I * 1024, 0);
-        };
-        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI { (one(ic<Is>{}), ...); }(
+            const int r = min(row, Skv - 1 - j * BN);
+            dma(ic<I>{}, (uint32_t)((r * kv_row + ch * 8) * 2), blk, lds);
+        }
+    };
+    auto load_block = [&](const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
+        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI { (load_piece(ic<Is>{}, src, dst, j, is_v), ...); }(
             std::make_integer_sequence<int, LOADS_PER_WAVE>{});
     };
     auto wait_loads = [&]() CPATTN_AI { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -247,8 +286,10 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     // MFMA slot body: the job list [QK jobs in (ks, kt) order] ++ [PV jobs in (t, dt)
     // order] (consecutive jobs use different accumulators), operand reads kReadAhead
     // jobs ahead, fenced so the compiler keeps that distance.
-    auto mfma_jobs = [&]<int KB, int VB, bool QK, bool PV>(ic<KB>, ic<VB>, std::bool_constant<QK>,
-                                                           std::bool_constant<PV>) CPATTN_AI {
+    constexpr int NPF = NQK < 8 ? NQK : 8;    // K fragments of the next M slot read in the softmax slot
+    u32x4 pre[NPF > 0 ? NPF : 1];
+    auto mfma_jobs = [&]<int KB, int VB, bool QK, bool PV, bool USE_PRE>(ic<KB>, ic<VB>, std::bool_constant<QK>,
+                                                           std::bool_constant<PV>, std::bool_constant<USE_PRE>, auto&& hook) CPATTN_AI {
         constexpr int J0 = QK ? 0 : NQK;
         constexpr int J1 = PV ? NQK + NPV : NQK;
         constexpr int NJ = J1 - J0;
@@ -261,7 +302,9 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
         u32x4 frag[NJ];
         auto rd = [&]<int I>(ic<I>) CPATTN_AI {
             constexpr int jid = J0 + I;
-            if constexpr (jid < NQK) {
+            if constexpr (USE_PRE && jid < NPF) {
+                frag[I] = pre[jid];
+            } else if constexpr (jid < NQK) {
                 constexpr int kt = jid % NKT, ks = jid / NKT;
                 frag[I] = read_k(ic<KB>{}, kt, ks);
             } else {
@@ -280,6 +323,7 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
                 oacc[dt] = mfma16<F16>(frag[I], pb[t], oacc[dt]);
             }
             __builtin_amdgcn_sched_barrier(0);
+            hook(ic<I>{}, ic<NJ>{});
         };
         [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI {
             (rd(ic<Is>{}), ...);
@@ -289,17 +333,39 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
             (step(ic<Is>{}), ...);
         }(std::make_integer_sequence<int, NJ>{});
     };
-    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1), with P = j & 1.
-    auto M = [&]<int R>(ic<R>, int j) CPATTN_AI {   // R = j % 3
-        constexpr int KB = R, VB = (R + 2) % 3;
+    // loads issued in M_j: this wave's pieces of K_{j+3} and V_{j+2}, into the buffers that
+    // M_{j-1} (both groups, slots before the previous barrier) released
+    auto issue_part = [&]<int R, int P>(ic<R>, ic<P>, int j) CPATTN_AI {
+        if constexpr (P < LOADS_PER_WAVE) {
+            if (j + 3 < nblk) load_piece(ic<P>{}, kp, Ks[(R + 3) % 4], j + 3, false);
+        } else {
+            if (j + 2 < nblk) load_piece(ic<P - LOADS_PER_WAVE>{}, vp, Vs[(R + 2) % 4], j + 2, true);
+        }
+    };
+    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1); R = j % 4.
+    auto M = [&]<int R, bool QK, bool PV, bool USE_PRE>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>,
+                                                      std::bool_constant<USE_PRE>, int j) CPATTN_AI {
+        constexpr int KB = R, VB = (R + 3) % 4;
+        auto hook = [&]<int I, int NJ>(ic<I>, ic<NJ>) CPATTN_AI {
+            constexpr int NP = 2 * LOADS_PER_WAVE;
+            constexpr int GAP = NJ / NP;
+            if constexpr (I % GAP == GAP / 2 && I / GAP < NP) {
+                issue_part(ic<R>{}, ic<I / GAP>{}, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
         __builtin_amdgcn_s_setprio(1);
-        if (j < nblk && j >= 1) mfma_jobs(ic<KB>{}, ic<VB>{}, std::true_type{}, std::true_type{});
-        else if (j < nblk) mfma_jobs(ic<KB>{}, ic<VB>{}, std::true_type{}, std::false_type{});
-        else if (j >= 1) mfma_jobs(ic<KB>{}, ic<VB>{}, std::false_type{}, std::true_type{});
+        mfma_jobs(ic<KB>{}, ic<VB>{}, std::bool_constant<QK>{}, std::bool_constant<PV>{}, std::bool_constant<USE_PRE>{}, hook);
         __builtin_amdgcn_s_setprio(0);
     };
     // SM_j: softmax of S_j -> P_j, row statistics, O *= alpha_j when some row raised its max.
-    auto SM = [&](int j) CPATTN_AI {
+    auto SM = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        if constexpr (NPF > 0) {
+            if (j + 1 < nblk) {
+#pragma unroll
+                for (int i = 0; i < NPF; ++i) pre[i] = read_k(ic<(R + 1) % 4>{}, i % NKT, i / NKT);
+            }
+        }
         if (j == nblk - 1 && (Skv % BN) != 0) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
@@ -346,16 +412,11 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
                 for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
         }
     };
-    // loads issued at global slot 2j: K_{j+2} and V_{j+1} (into the buffers M_{j-1} released)
-    auto issue = [&]<int R>(ic<R>, int j) CPATTN_AI {
-        if (j + 2 < nblk) load_block(kp, Ks[(R + 2) % 3], j + 2, false);
-        if (j + 1 < nblk) load_block(vp, Vs[(R + 1) % 3], j + 1, true);
-    };
-    // Wait until at most this wave's latest issue of loads (issue(jl)) is in flight.  The
-    // count is exact only when that issue was a full one (K and V); near the end, where it
-    // carried fewer loads, wait for everything.
+    // Wait until at most this wave's latest issue of loads (made in M_jl) is in flight: exact
+    // while that issue was a full one (K and V); near the end, where issues carry fewer loads,
+    // wait for everything.
     auto wait_older = [&](int jl) CPATTN_AI {
-        if (jl + 2 < nblk)
+        if (jl + 3 < nblk)
             asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS_PER_WAVE) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -363,41 +424,53 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
 
     load_block(kp, Ks[0], 0, false);
     if (nblk > 1) load_block(kp, Ks[1], 1, false);
+    if (nblk > 2) load_block(kp, Ks[2], 2, false);
     load_block(vp, Vs[0], 0, true);
+    if (nblk > 1) load_block(vp, Vs[1], 1, true);
     wait_loads();
     __syncthreads();
 
     // Both groups run M_0, SM_0, M_1, SM_1, ..., M_nblk; group 1 starts one slot late (an
-    // extra barrier up front; group 0 adds one at the end).  Each wave issues its share of
-    // (K_{j+2}, V_{j+1}) at the start of a softmax slot -- group 1 at global slot 2j, group 0
-    // at 2j+1 -- into the buffers last read by M_{j-1} (slots 2j-2, 2j-1).  Before the
-    // barrier ending a softmax slot a wave waits for all but its latest issue, so both
-    // shares are in LDS by the end of slot 2j+3, in time for M_{j+2} (slot 2j+4).  The slot
-    // barrier itself does not wait for outstanding memory operations.
+    // extra barrier up front; group 0 adds one at the end), so on every SIMD one wave is in
+    // an MFMA slot while the other is in a softmax slot.  A wave issues its pieces of
+    // (K_{j+3}, V_{j+2}) inside its M_j slot, into the buffers of K_{j-1} and V_{j-2}, which
+    // M_{j-1} of both groups finished reading before the previous barrier.  Before every
+    // slot barrier a wave waits for all but its latest issue, so the blocks issued in M_{j-2}
+    // are in LDS by the start of slot 2j+1: SM_j prefetches K_{j+1} fragments from there,
+    // and M_{j+1} reads K_{j+1}, V_j.  The slot barrier itself does not wait for memory.
     auto slot_barrier = [&]() CPATTN_AI { asm volatile("s_barrier" ::: "memory"); };
-    auto body = [&]<int R>(ic<R>, int j) CPATTN_AI {
-        M(ic<R>{}, j);
+    auto body = [&]<int R, bool QK, bool PV, bool USE_PRE>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>,
+                                                         std::bool_constant<USE_PRE>, int j) CPATTN_AI {
+        M(ic<R>{}, std::bool_constant<QK>{}, std::bool_constant<PV>{}, std::bool_constant<USE_PRE>{}, j);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_older(j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
-        if (group != 0) issue(ic<(R + 1) % 3>{}, j + 1);
-        else issue(ic<R>{}, j);
-        if (j < nblk) SM(j);
-        wait_older(group != 0 ? j + 1 : j);
+        if constexpr (QK) SM(ic<R>{}, j);
+        wait_older(j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
     };
-    if (group != 0) {
-        issue(ic<0>{}, 0);
-        slot_barrier();
+    using T = std::true_type;
+    using F = std::false_type;
+    if (group != 0) slot_barrier();
+    body(ic<0>{}, T{}, F{}, F{}, 0);
+    int j = 1;
+    for (; j + 3 < nblk; j += 4) {
+        body(ic<1>{}, T{}, T{}, T{}, j);
+        body(ic<2>{}, T{}, T{}, T{}, j + 1);
+        body(ic<3>{}, T{}, T{}, T{}, j + 2);
+        body(ic<0>{}, T{}, T{}, T{}, j + 3);
     }
-    int j = 0;
-    for (; j + 2 <= nblk; j += 3) {
-        body(ic<0>{}, j);
-        body(ic<1>{}, j + 1);
-        body(ic<2>{}, j + 2);
+    if (j < nblk) body(ic<1>{}, T{}, T{}, T{}, j);
+    if (j + 1 < nblk) body(ic<2>{}, T{}, T{}, T{}, j + 1);
+    if (j + 2 < nblk) body(ic<3>{}, T{}, T{}, T{}, j + 2);
+    switch (nblk & 3) {      // M_nblk: the last PV product only
+        case 0: body(ic<0>{}, F{}, T{}, F{}, nblk); break;
+        case 1: body(ic<1>{}, F{}, T{}, F{}, nblk); break;
+        case 2: body(ic<2>{}, F{}, T{}, F{}, nblk); break;
+        default: body(ic<3>{}, F{}, T{}, F{}, nblk); break;
     }
-    if (j <= nblk) body(ic<0>{}, j);
-    if (j + 1 <= nblk) body(ic<1>{}, j + 1);
     if (group == 0) slot_barrier();
 
     // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2; a piece goes to the workspace, an

@@ -123,6 +123,9 @@ def test_attn_fwd_ex_validation(L):
     assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR, q=None) == _lib.E_NULL
     assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR, o=A + 16) == _lib.E_ALIAS
     assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR | _lib.FLAG_ACCUMULATE, od=_lib.BF16) == _lib.E_DTYPE
+    # a token row of H * D >= 2^25 elements does not fit the kernels' 32-bit block offsets
+    # (one row of q/k/v/o: 64 MiB each, inside the fake buffers' 256 MiB spacing)
+    assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR, H=1 << 19, Sq=1, Skv=1, ws=None, ws_bytes=0) == _lib.E_SHAPE
     # accumulate needs bf16 inputs and an f32 accumulator
     assert fwd_ex(L, flags=_lib.FLAG_ACCUMULATE, od=_lib.BF16) == _lib.E_DTYPE
     assert fwd_ex(L, flags=_lib.FLAG_ACCUMULATE, i=_lib.F32, od=_lib.F32) == _lib.E_DTYPE
