@@ -55,9 +55,11 @@
 //    MFMAs ahead;
 //  - a CU's vector-memory path accepts one 1 KB global->LDS load per ~32
 //    clocks and a wave stalls at issue until its loads are taken.  A softmax
-//    slot that issued loads would stall on the critical path, so each wave
-//    issues its four pieces inside its MFMA slot, spread between MFMAs, three
-//    blocks ahead of use (four buffers).
+//    slot that issued all its loads would stall on the critical path, so each
+//    wave issues three of its four pieces inside its MFMA slot, spread between
+//    MFMAs, and the fourth at the end of its softmax slot, where it would
+//    otherwise wait at the barrier; loads run three blocks ahead of use (four
+//    buffers).
 // Slot barriers are plain s_barrier: each wave waits only for its own older
 // loads (vmcnt) before arriving.
 //
@@ -333,8 +335,11 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
             (step(ic<Is>{}), ...);
         }(std::make_integer_sequence<int, NJ>{});
     };
-    // loads issued in M_j: this wave's pieces of K_{j+3} and V_{j+2}, into the buffers that
-    // M_{j-1} (both groups, slots before the previous barrier) released
+    // Loads issued for block j: this wave's pieces of K_{j+3} and V_{j+2}, into the buffers
+    // that M_{j-1} (both groups, slots before the previous barrier) released.  The first
+    // NP_M pieces go between the MFMAs of M_j, the last one at the end of SM_j, where the
+    // softmax wave would otherwise wait at the barrier.
+    constexpr int NP_M = 2 * LOADS_PER_WAVE - 1;
     auto issue_part = [&]<int R, int P>(ic<R>, ic<P>, int j) CPATTN_AI {
         if constexpr (P < LOADS_PER_WAVE) {
             if (j + 3 < nblk) load_piece(ic<P>{}, kp, Ks[(R + 3) % 4], j + 3, false);
@@ -347,9 +352,8 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
                                                       std::bool_constant<USE_PRE>, int j) CPATTN_AI {
         constexpr int KB = R, VB = (R + 3) % 4;
         auto hook = [&]<int I, int NJ>(ic<I>, ic<NJ>) CPATTN_AI {
-            constexpr int NP = 2 * LOADS_PER_WAVE;
-            constexpr int GAP = NJ / NP;
-            if constexpr (I % GAP == GAP / 2 && I / GAP < NP) {
+            constexpr int GAP = NJ / NP_M;
+            if constexpr (I % GAP == GAP / 2 && I / GAP < NP_M) {
                 issue_part(ic<R>{}, ic<I / GAP>{}, j);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -446,7 +450,11 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
         wait_older(j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
-        if constexpr (QK) SM(ic<R>{}, j);
+        if constexpr (QK) {
+            SM(ic<R>{}, j);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_part(ic<R>{}, ic<NP_M>{}, j);
+        }
         wait_older(j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
