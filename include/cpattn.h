@@ -190,7 +190,8 @@ cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, vo
  * no recipe; this one runs both products on gfx950's fp8 matrix cores (twice the bf16
  * rate) with f32 scores and softmax state, and rounds the softmax weights to E4M3 (as
  * p * 2^7, p <= 2) for the PV product.  D = 128 only (CPATTN_E_HEADDIM); scales finite
- * and > 0 (CPATTN_E_SCALE); flags: 0 or CPATTN_FLAG_SEQ_MAJOR (else CPATTN_E_FLAGS);
+ * and > 0 (CPATTN_E_SCALE); flags: 0 or CPATTN_FLAG_SEQ_MAJOR (else CPATTN_E_FLAGS;
+ * sequence-major needs H * D < 2^25, else CPATTN_E_SHAPE);
  * Skv = 0 gives O = 0, LSE = -inf.  Other checks as for cpattn_attn_fwd.
  */
 cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,

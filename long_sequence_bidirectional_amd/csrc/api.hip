@@ -292,6 +292,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, co
     cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, scale, 32, &c);
     if (st != CPATTN_OK) return st;
     if (D != 128) return CPATTN_E_HEADDIM;
+    if (seq_major && H * D >= (int64_t(1) << 25)) return CPATTN_E_SHAPE;   // 32-bit block offsets
     for (float s : {q_scale, k_scale, v_scale})
         if (!(s > 0.f) || !isfinite(s)) return CPATTN_E_SCALE;
     if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || (Skv && (!aligned16(k) || !aligned16(v))))

@@ -8,10 +8,12 @@
 // state are f32, the softmax weights are rounded to E4M3 for the PV product, and O
 // is stored as bf16 or f32.  D = 128.
 //
-// Work split and schedule are those of the bf16 kernel: 8 waves, 256 query rows per
+// Work split and schedule follow the bf16 kernel: 8 waves, 256 query rows per
 // workgroup, waves w and w+4 on one SIMD alternating an MFMA slot (4 QK + 4 PV MFMAs
-// per 64-key block) with a softmax slot, K/V through three LDS buffers by direct
-// global->LDS loads, Q^T in registers.
+// per 64-key block) with a softmax slot, K/V through four LDS buffers by direct
+// global->LDS loads issued inside the MFMA slot three blocks ahead (the softmax slot,
+// twice as long as the MFMA slot here, is the critical one and issues none), Q^T in
+// registers.
 //
 // Operand layouts of the 32x32x64 fp8 MFMA: lane (row/column l%32, half h = l/32)
 // holds 32 bytes of its row of A (column of B); byte j of half h of A meets byte j
@@ -31,8 +33,9 @@
 // Softmax: t = s * c with c = scale * log2(e) * q_scale * k_scale; the running max is
 // raised only when a block's max exceeds it by more than 1, so p = exp2(t - m) <= 2;
 // the weights enter the PV product as E4M3 of p * 2^7 (<= 256 < 448, and typical
-// weights stay in E4M3's normal range), O = sum(p8 v) * v_scale / (2^7 * l) with the
-// row sum l of the unrounded f32 weights, LSE = (m + log2 l) * ln 2.
+// weights stay in E4M3's normal range), computed directly as exp2(t - m + 7); the row
+// sum l' of these unrounded f32 values carries the same 2^7, so O = sum(p8 v) * v_scale
+// / l' and LSE = (m + log2 l' - 7) * ln 2.
 #include <utility>
 
 #include "common.h"
@@ -54,9 +57,9 @@ using ic = std::integral_constant<int, I>;
 constexpr int kD = 128;
 constexpr int kBM = kAttnTileRows;   // 256 query rows per workgroup
 constexpr int kBN = 64;              // keys per block
-constexpr int kNBUF = 3;
+constexpr int kNBUF = 4;
 constexpr float kRaiseTh = 1.0f;     // raise m only when a block max exceeds it by more than 1
-constexpr float kPScale = 128.0f;    // p enters the PV product as E4M3(p * 2^7)
+constexpr float kPScaleLog2 = 7.0f;  // p enters the PV product as E4M3(p * 2^7)
 
 // stored 16-byte chunk of logical chunk c of row r
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
                                                            const uint8_t* __restrict__ v, void* __restrict__ o,
                                                            float* __restrict__ lse, int Sq, int Skv, int nQt, int H,
                                                            Strides sq, Strides skv, Strides so, int total,
-                                                           int per_xcd, float c, float out_scale) {
+                                                           int per_xcd, float c, float v_scale) {
     constexpr int D = kD, BN = kBN;
     constexpr int NKS = D / 64;            // k-steps of QK (64 d each)
     constexpr int NDT = D / 32;            // 32-wide d tiles of O^T
@@ -95,6 +98,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     const int qt = logical - bh * nQt;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
@@ -111,14 +115,29 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     const int qrow = qt * kBM + wave * 32 + l32;
     const int nblk = (Skv + BN - 1) / BN;
 
-    // one 1 KB piece per wave per tensor: rows 8*wave .. 8*wave+7 of the block
+    // One 1 KB piece per wave per tensor: LDS rows 8*wave .. 8*wave+7 of the block.  A load is
+    // the block's wave-uniform base (SGPRs) plus a per-lane byte offset that is the same for
+    // every full block; the last, partial block clamps its rows.  M0 holds the LDS base;
+    // nothing else in this kernel uses M0, so the asm sets it itself.
+    const int lrow = wave_u * RPP + lane / 8;                         // LDS row of this lane
+    const int lch = (lane % 8) ^ swz8(lrow);                          // logical chunk it moves
+    const uint32_t koffb = (uint32_t)(swap23(lrow) * kv_row + lch * 16);   // K row swap23(lrow)
+    const uint32_t voffb = (uint32_t)(lrow * kv_row + lch * 16);
     auto load_block = [&](const uint8_t* src, uint8_t* dst, int j, bool is_k) CPATTN_AI {
-        const int row = wave * RPP + lane / 8;                       // LDS row
-        const int key = is_k ? swap23(row) : row;                    // key stored there
-        const int ch = (lane % 8) ^ swz8(row);                       // logical chunk of this lane
-        const int r = min(j * BN + key, Skv - 1);
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(void, src + r * kv_row + ch * 16),
-                                         LDS_PTR(void, dst + wave * 1024), 16, 0, 0);
+        const uint32_t lds = (uint32_t)(uintptr_t)LDS_PTR(void, dst + wave_u * 1024);
+        const uint8_t* blk = src + (int64_t)j * BN * kv_row;
+        uint32_t off;
+        if ((j + 1) * BN <= Skv) {
+            off = is_k ? koffb : voffb;
+        } else {
+            const int key = min(is_k ? swap23(lrow) : lrow, Skv - 1 - j * BN);
+            off = (uint32_t)(key * kv_row + lch * 16);
+        }
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0"
+                     :: "v"(off), "s"(blk), "s"(lds) : "memory", "m0");
+#pragma clang diagnostic pop
     };
 
     // Q^T operand: lane (query l32, half hh), k-step ks: bytes d = 64 ks + 32 hh .. +31
@@ -165,11 +184,20 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     i32x8 pb;                  // P^T bytes: j = 16 kt + i
     float m_run = -INFINITY, l_run = 0.f, alpha = 1.f;
 
-    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1)
-    auto M = [&]<int R>(ic<R>, int j) CPATTN_AI {
-        constexpr int KB = R, VB = (R + 2) % 3;
+    // Loads for block j, issued inside M_j: this wave's pieces of K_{j+3} and V_{j+2}, into the
+    // buffers of K_{j-1} and V_{j-2}, which M_{j-1} of both groups finished reading before the
+    // previous barrier.  The softmax slot, the critical one here, issues none.
+    auto issue_k = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        if (j + 3 < nblk) load_block(kp, Ks[(R + 3) % 4], j + 3, true);
+    };
+    auto issue_v = [&]<int R>(ic<R>, int j) CPATTN_AI {
+        if (j + 2 < nblk) load_block(vp, Vs[(R + 2) % 4], j + 2, false);
+    };
+    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1); R = j % 4
+    auto M = [&]<int R, bool QK, bool PV>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>, int j) CPATTN_AI {
+        constexpr int KB = R, VB = (R + 3) % 4;
         __builtin_amdgcn_s_setprio(1);
-        if (j < nblk) {
+        if constexpr (QK) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -177,11 +205,27 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma8(read_k(ic<KB>{}, kt, ks), qreg[ks], s[kt]);
+                for (int kt = 0; kt < NKT; ++kt) {
+                    s[kt] = mfma8(read_k(ic<KB>{}, kt, ks), qreg[ks], s[kt]);
+                    if (ks == 0 && kt == 1) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue_k(ic<R>{}, j);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
         }
-        if (j >= 1) {
+        if constexpr (PV) {
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma8(read_vt(ic<VB>{}, dt), pb, oacc[dt]);
+            for (int dt = 0; dt < NDT; ++dt) {
+                oacc[dt] = mfma8(read_vt(ic<VB>{}, dt), pb, oacc[dt]);
+                if (dt == 1 && QK) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_v(ic<R>{}, j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else if constexpr (QK) {
+            issue_v(ic<R>{}, j);
         }
         __builtin_amdgcn_s_setprio(0);
     };
@@ -206,6 +250,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
         const float m_new = raise ? mx : m_run;
         alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
+        const float mb = kPScaleLog2 - m_new;   // weights come out scaled by 2^7
         float psum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
@@ -214,11 +259,11 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
                 float p[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    p[e] = exp2_fast(__builtin_fmaf(s[kt][w * 4 + e], c, -m_new));
+                    p[e] = exp2_fast(__builtin_fmaf(s[kt][w * 4 + e], c, mb));
                     psum += p[e];
                 }
-                int word = pack_fp8x2<false>(p[0] * kPScale, p[1] * kPScale, 0);
-                word = pack_fp8x2<true>(p[2] * kPScale, p[3] * kPScale, word);
+                int word = pack_fp8x2<false>(p[0], p[1], 0);
+                word = pack_fp8x2<true>(p[2], p[3], word);
                 pb[kt * 4 + w] = word;
             }
         l_run = l_run * alpha + psum;
@@ -231,51 +276,60 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
                 for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
         }
     };
-    auto issue = [&]<int R>(ic<R>, int j) CPATTN_AI {
-        if (j + 2 < nblk) load_block(kp, Ks[(R + 2) % 3], j + 2, true);
-        if (j + 1 < nblk) load_block(vp, Vs[(R + 1) % 3], j + 1, false);
-    };
-    // wait until at most this wave's latest issue (two loads when full) is in flight
+    // wait until at most this wave's latest issue (two loads when full) is in flight: then
+    // the blocks issued in M_{j-2} are complete before the barrier ahead of slot 2j+1
     auto wait_older = [&](int jl) CPATTN_AI {
-        if (jl + 2 < nblk) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        if (jl + 3 < nblk) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
     load_block(kp, Ks[0], 0, true);
     if (nblk > 1) load_block(kp, Ks[1], 1, true);
+    if (nblk > 2) load_block(kp, Ks[2], 2, true);
     load_block(vp, Vs[0], 0, false);
+    if (nblk > 1) load_block(vp, Vs[1], 1, false);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    // Both groups run M_0, SM_0, ..., M_nblk; group 1 one slot behind (an extra barrier up
+    // front; group 0 adds one at the end).
     auto slot_barrier = [&]() CPATTN_AI { asm volatile("s_barrier" ::: "memory"); };
-    auto body = [&]<int R>(ic<R>, int j) CPATTN_AI {
-        M(ic<R>{}, j);
+    auto body = [&]<int R, bool QK, bool PV>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>, int j) CPATTN_AI {
+        M(ic<R>{}, std::bool_constant<QK>{}, std::bool_constant<PV>{}, j);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_older(j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
-        if (group != 0) issue(ic<(R + 1) % 3>{}, j + 1);
-        else issue(ic<R>{}, j);
-        if (j < nblk) SM(j);
-        wait_older(group != 0 ? j + 1 : j);
+        if constexpr (QK) SM(j);
+        wait_older(j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
     };
-    if (group != 0) {
-        issue(ic<0>{}, 0);
-        slot_barrier();
+    using T = std::true_type;
+    using F = std::false_type;
+    if (group != 0) slot_barrier();
+    body(ic<0>{}, T{}, F{}, 0);
+    int j = 1;
+    for (; j + 3 < nblk; j += 4) {
+        body(ic<1>{}, T{}, T{}, j);
+        body(ic<2>{}, T{}, T{}, j + 1);
+        body(ic<3>{}, T{}, T{}, j + 2);
+        body(ic<0>{}, T{}, T{}, j + 3);
     }
-    int j = 0;
-    for (; j + 2 <= nblk; j += 3) {
-        body(ic<0>{}, j);
-        body(ic<1>{}, j + 1);
-        body(ic<2>{}, j + 2);
+    if (j < nblk) body(ic<1>{}, T{}, T{}, j);
+    if (j + 1 < nblk) body(ic<2>{}, T{}, T{}, j + 1);
+    if (j + 2 < nblk) body(ic<3>{}, T{}, T{}, j + 2);
+    switch (nblk & 3) {      // M_nblk: the last PV product only
+        case 0: body(ic<0>{}, F{}, T{}, nblk); break;
+        case 1: body(ic<1>{}, F{}, T{}, nblk); break;
+        case 2: body(ic<2>{}, F{}, T{}, nblk); break;
+        default: body(ic<3>{}, F{}, T{}, nblk); break;
     }
-    if (j <= nblk) body(ic<0>{}, j);
-    if (j + 1 <= nblk) body(ic<1>{}, j + 1);
     if (group == 0) slot_barrier();
 
     const float l_tot = sum_across_halves(l_run);
     if (qrow < Sq) {
-        const float inv = l_tot > 0.f ? out_scale / l_tot : 0.f;     // v_scale / (2^7 l)
+        const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;       // l carries the 2^7 of the weights
         const int64_t orow = o_base + qrow * o_row;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -290,7 +344,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
                     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + d0) =
                         u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
             }
-        if (hh == 0) lse[(int64_t)bh * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        if (hh == 0)
+            lse[(int64_t)bh * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot) - kPScaleLog2) * kLn2 : -INFINITY;
     }
 }
 
@@ -300,11 +355,11 @@ hipError_t launch_fp8_typed(const AttnFp8Args& a) {
     const int64_t total = a.BH * nQt;
     const int per_xcd = (int)((total + kNumXcd - 1) / kNumXcd);
     const float c = (float)((double)a.scale * 1.4426950408889634 * (double)a.q_scale * (double)a.k_scale);
-    const float out_scale = (float)((double)a.v_scale / (double)kPScale);
+
     hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32, SEQ>), dim3(per_xcd * kNumXcd), dim3(512), 0, a.stream,
                        static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
                        static_cast<const uint8_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)a.H, a.sq,
-                       a.skv, a.so, (int)total, per_xcd, c, out_scale);
+                       a.skv, a.so, (int)total, per_xcd, c, a.v_scale);
     return hipGetLastError();
 }
 

@@ -246,6 +246,8 @@ def test_attn_fwd_fp8_validation(L):
     assert fp8(L, vs=float("inf")) == _lib.E_SCALE
     assert fp8(L, flags=_lib.FLAG_ACCUMULATE) == _lib.E_FLAGS
     assert fp8(L, flags=4) == _lib.E_FLAGS
+    # a token row of H * D >= 2^25 bytes does not fit the kernel's 32-bit block offsets
+    assert fp8(L, flags=_lib.FLAG_SEQ_MAJOR, H=1 << 18, Sq=1, Skv=1) == _lib.E_SHAPE
     assert fp8(L, o=E + 16) == _lib.E_ALIGN or fp8(L, o=E + 16) == _lib.E_ALIAS
     assert fp8(L, o=A + 1024) == _lib.E_ALIAS          # o on top of q
     assert fp8(L, lse=C + 64) == _lib.E_ALIAS          # lse on top of v
