@@ -1,0 +1,89 @@
+"""GPU parity at every small key-block count and around each 64-key block edge.
+
+The attention kernels stream K/V in 64-key blocks through four LDS buffers: a
+prologue loads the first three K blocks and two V blocks, each MFMA slot issues
+the loads three blocks ahead, a remainder runs the last one to three blocks of
+the unrolled loop, and a final slot does the last PV product alone.  Key counts
+1..6 blocks (and one key either side of each block edge) exercise every such
+path, in the bf16, fp16 and fp8 kernels, with and without a ragged query tile;
+the split path is checked with pieces of four to five blocks.  Oracle: exact
+fp64 attention of the same inputs; bounds as in the other parity tests.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import long_sequence_bidirectional_amd as cp
+from long_sequence_bidirectional_amd import inputs
+from helpers import assert_bf16_parity, dev_bf16, f64_of_bf16, host64, log, scale_of
+from test_gpu_fp8 import check_fp8, dev8
+from test_gpu_p4 import assert_f16_parity
+
+pytestmark = pytest.mark.gpu
+
+KEYS = [1, 2, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 319, 320, 321, 383, 384]
+
+
+@pytest.mark.parametrize("Skv", KEYS)
+@pytest.mark.parametrize("D", [128, 64])
+def test_bf16_block_counts(Skv, D):
+    B, H, Sq = 1, 2, 300
+    log(f"case: bf16 B{B} H{H} Sq{Sq} Skv{Skv} D{D}")
+    seed = 8000 + Skv + D
+    qb = inputs.random_bf16((B, H, Sq, D), seed)
+    kb = inputs.random_bf16((B, H, Skv, D), seed + 1)
+    vb = inputs.random_bf16((B, H, Skv, D), seed + 2)
+    o, lse = cp.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+    assert_bf16_parity(host64(o), host64(lse), O, L, f"bf16 Skv={Skv} D={D}")
+
+
+@pytest.mark.parametrize("Skv", KEYS)
+def test_f16_block_counts(Skv):
+    B, H, Sq, D = 1, 2, 300, 128
+    log(f"case: fp16 B{B} H{H} Sq{Sq} Skv{Skv} D{D}")
+    seed = 8100 + Skv
+    q = inputs.random_f16((B, H, Sq, D), seed)
+    k = inputs.random_f16((B, H, Skv, D), seed + 1)
+    v = inputs.random_f16((B, H, Skv, D), seed + 2)
+    o, lse = cp.attn_fwd(*(torch.from_numpy(x).cuda() for x in (q, k, v)))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), scale_of(D))
+    assert_f16_parity(host64(o), host64(lse), O, L, f"fp16 Skv={Skv}")
+
+
+@pytest.mark.parametrize("Skv", KEYS)
+def test_fp8_block_counts(Skv):
+    B, H, Sq, D = 1, 2, 300, 128
+    log(f"case: fp8 B{B} H{H} Sq{Sq} Skv{Skv} D{D}")
+    seed = 8200 + Skv
+    q8 = inputs.random_e4m3((B, H, Sq, D), seed)
+    k8 = inputs.random_e4m3((B, H, Skv, D), seed + 1)
+    v8 = inputs.random_e4m3((B, H, Skv, D), seed + 2)
+    o, lse = cp.attn_fwd_fp8(dev8(q8), dev8(k8), dev8(v8))
+    torch.cuda.synchronize()
+    check_fp8(q8, k8, v8, 1.0, 1.0, 1.0, 1.0 / math.sqrt(D), o, lse, f"fp8 Skv={Skv}")
+
+
+@pytest.mark.parametrize("Skv", [513, 577, 640, 704, 768])
+def test_split_short_pieces(Skv):
+    """Few tiles (all in the device's last, partial wave) and 8-10 key blocks: the planner cuts
+    each tile into two or three pieces of four to five blocks, so every piece runs the shortest pipelines."""
+    B, H, Sq, D = 1, 2, 300, 128
+    seed = 8300 + Skv
+    qb = inputs.random_bf16((B, H, Sq, D), seed)
+    kb = inputs.random_bf16((B, H, Skv, D), seed + 1)
+    vb = inputs.random_bf16((B, H, Skv, D), seed + 2)
+    n = cp.attn_fwd_workspace_size(B, H, Sq, Skv, D)
+    tiles, pieces, _ = cp.attn_fwd_split_plan(B, H, Sq, Skv, D, 256, n)
+    log(f"case: split B{B} H{H} Sq{Sq} Skv{Skv} D{D}: workspace {n} B, {tiles} tiles x {pieces} pieces")
+    assert tiles > 0 and pieces >= 2
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+    o, lse = cp.attn_fwd_ex(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), workspace=ws)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+    assert_bf16_parity(host64(o), host64(lse), O, L, f"split Skv={Skv}")
