@@ -24,6 +24,7 @@ import json
 import math
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -83,6 +84,20 @@ def parse():
 
 def elapsed_ms(pairs):
     return [a.elapsed_time(b) for a, b in pairs]
+
+
+def smi_sample():
+    """(socket power W, mean gfx clock MHz) from one amd-smi reading, or None.  The kernel runs at
+    the board's power limit, so the clock it ran at is part of the measurement."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clks = [float(g["clock"][f"gfx_{i}"]["clk"]["value"]) for i in range(8) if f"gfx_{i}" in g["clock"]]
+        return float(g["power"]["socket_power"]["value"]), sum(clks) / len(clks)
+    except Exception:
+        return None
 
 
 def cpu_baseline(budget_s: float):
@@ -187,19 +202,26 @@ def main():
     ev_self = []
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    # one power / clock reading taken while the timed steps run (host thread, no GPU work)
+    smi = []
+    sampler = threading.Thread(target=lambda: (time.sleep(0.8), smi.append(smi_sample())), daemon=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
+    sampler.start()
     for _ in range(args.steps):
         step(ev_self)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    sampler.join(timeout=30)
+    power_clock = smi[0] if smi else None
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
     value = flops_step / (ms_step * 1e-3) / 1e12
     self_ms = elapsed_ms(ev_self)
     self_avg = sum(self_ms) / len(self_ms)
+    self_sorted = sorted(self_ms)
     achieved = flops_self / (self_avg * 1e-3) / 1e12
 
     traffic, counters = measured_counters(args.traffic)
@@ -227,6 +249,10 @@ def main():
                      "kernel": "attn_fwd_mfma_kernel<128,bf16,o bf16,head-major> + merge_pieces_kernel<bf16> "
                                "(self-attention S=44160; the events bracket both)",
                      "avg_launch_ms": round(self_avg, 4), "launches": len(self_ms),
+                     "median_launch_ms": round(self_sorted[len(self_sorted) // 2], 4),
+                     "min_launch_ms": round(self_sorted[0], 4), "max_launch_ms": round(self_sorted[-1], 4),
+                     "socket_power_w": power_clock[0] if power_clock else None,
+                     "gfx_clock_mhz": round(power_clock[1]) if power_clock else None,
                      "split": split_of(cp, H, S, S, D, ws_self),
                      "counters": counters},
         "wall_s_timed": round(wall, 3),
