@@ -315,8 +315,26 @@ def profile_pass(cp, torch, q, k, v):
     for a, b in zip(shards, sends):
         cp.ulysses_unpack(b, P, cp.SEQ_TO_HEAD, dst=a.view(1, H // P, S_L * P, D))
     torch.cuda.synchronize()
+    del shards, sends
+    # the fp8 self-attention (E4M3 of N(0,1) draws, made on the device) and the QK-RMSNorm
+    # prologue over the attention sample's K [56320, 32, 128] fp16 (461 MB each way)
+    q8, k8, v8 = (torch.randn((1, H, inputs.S_VIDEO, D), device="cuda").to(torch.float8_e4m3fn)
+                  for _ in range(3))
+    o8 = torch.empty((1, H, inputs.S_VIDEO, D), dtype=torch.bfloat16, device="cuda")
+    l8 = torch.empty((1, H, inputs.S_VIDEO), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    cp.attn_fwd_fp8(q8, k8, v8, o=o8, lse=l8)
+    torch.cuda.synchronize()
+    del q8, k8, v8, o8, l8
+    x = torch.randn((1, inputs.P4_SEQ, inputs.P4_HEADS, D), device="cuda").to(torch.float16)
+    w = torch.randn((D,), device="cuda").to(torch.float16)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    cp.qk_rmsnorm(x, w, 1e-6, D ** -0.25, out=y)
+    torch.cuda.synchronize()
     print(f"profile pass done; calibration copy {CALIB_SHAPE[1] * CALIB_SHAPE[2] * CALIB_SHAPE[3] * 2} bytes "
-          "read and written; 12 cold merges, packs and unpacks", flush=True)
+          "read and written; 12 cold merges, packs and unpacks; fp8 self-attention; QK-RMSNorm of "
+          f"{x.numel() * 2} bytes", flush=True)
 
 
 def secondary_rows(cp, torch, q, k, v, stream):

@@ -26,9 +26,9 @@
 // group, lane pair (2i, 2i+1) addresses row r0 + i (bytes 0-7 and 8-15 of a 16-byte
 // column block) and lane L receives column L of the 8 rows.
 //
-// Rows are 128 bytes; 16-byte chunks are XOR-swizzled by (row >> 1) & 7 so that both
-// the K reads (16 rows x one chunk) and the transposing V reads (8 rows x one chunk)
-// hit distinct banks.
+// Rows are 128 bytes; 16-byte chunks are XOR-swizzled by a permutation of the row pair
+// (swz8 below) so that both the K reads (16 rows x one chunk) and the transposing V reads
+// (8 rows x two chunks per 32 lanes) hit distinct banks.
 //
 // Softmax: t = s * c with c = scale * log2(e) * q_scale * k_scale; the running max is
 // raised only when a block's max exceeds it by more than 1, so p = exp2(t - m) <= 2;
@@ -61,8 +61,16 @@ constexpr int kNBUF = 4;
 constexpr float kRaiseTh = 1.0f;     // raise m only when a block max exceeds it by more than 1
 constexpr float kPScaleLog2 = 7.0f;  // p enters the PV product as E4M3(p * 2^7)
 
-// stored 16-byte chunk of logical chunk c of row r
-__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+// Stored 16-byte chunk of logical chunk c of row r is c ^ swz8(r), with swz8 a permutation of
+// the row pair u = (r >> 1) & 7: u -> ((u & 3) << 1) | (u >> 2).  K reads (16 consecutive rows,
+// one chunk): the 8 row pairs take 8 distinct values.  Transposing V reads (per 32 lanes: 8
+// consecutive rows 8m..8m+7 x the two chunks 2dt, 2dt+1): the four row pairs take values of
+// distinct s >> 1, so the chunk pairs {2dt ^ s, (2dt + 1) ^ s} are disjoint.  Both hit 64
+// distinct banks.
+__device__ __forceinline__ int swz8(int r) {
+    const int u = (r >> 1) & 7;
+    return ((u & 3) << 1) | (u >> 2);
+}
 // LDS row of K that holds key (row) r of the block, and back: swap bits 2 and 3
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
