@@ -45,9 +45,13 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float16 or float32)")
 
 
-def _dev(t, name):
+def _dev(t, name, device=None):
+    """Device pointer of a contiguous device tensor (on `device` when given).  The C ABI cannot
+    tell a host or strided buffer from a device one, so every pointer passes through here."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
@@ -83,8 +87,9 @@ def _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major=False):
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if tuple(o.shape) != o_shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
         raise ValueError(f"o must be {o_shape} and lse float32 [B,H,Sq]")
-    args = (_dev(q, "q"), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None, _dev(o, "o"),
-            _dev(lse, "lse"), B, H, Sq, Skv, D, float(scale), _dtype_code(q), _dtype_code(o))
+    dv = q.device
+    args = (_dev(q, "q"), _dev(k, "k", dv) if Skv else None, _dev(v, "v", dv) if Skv else None,
+            _dev(o, "o", dv), _dev(lse, "lse", dv), B, H, Sq, Skv, D, float(scale), _dtype_code(q), _dtype_code(o))
     return o, lse, args
 
 
@@ -138,8 +143,10 @@ def attn_fwd_fp8(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, o=None, lse=Non
     if tuple(o.shape) != o_shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
         raise ValueError(f"o must be {o_shape} and lse float32 [B,H,Sq]")
     flags = FLAG_SEQ_MAJOR if seq_major else 0
-    st = lib().cpattn_attn_fwd_fp8(_dev(q, "q"), k.data_ptr() if Skv else None, v.data_ptr() if Skv else None,
-                                   _dev(o, "o"), _dev(lse, "lse"), B, H, Sq, Skv, D, float(scale), float(q_scale),
+    dv = q.device
+    st = lib().cpattn_attn_fwd_fp8(_dev(q, "q"), _dev(k, "k", dv) if Skv else None,
+                                   _dev(v, "v", dv) if Skv else None, _dev(o, "o", dv), _dev(lse, "lse", dv),
+                                   B, H, Sq, Skv, D, float(scale), float(q_scale),
                                    float(k_scale), float(v_scale), _dtype_code(o), flags, _stream(stream))
     check("cpattn_attn_fwd_fp8", st)
     return o, lse
@@ -205,10 +212,11 @@ def ring_attn_fwd(q, k_chunks, v_chunks, o=None, lse=None, o_work=None, lse_work
         raise ValueError("give both o_work and lse_work, or neither")
     if o_work is None and use_work:   # scratch for the key-range split of partial waves
         o_work, lse_work = torch.empty_like(o), torch.empty_like(lse)
-    st = lib().cpattn_ring_attn_fwd(_dev(q, "q"), k_chunks.data_ptr() if Skv_c else None,
-                                    v_chunks.data_ptr() if Skv_c else None, _dev(o, "o"), _dev(lse, "lse"),
-                                    _dev(o_work, "o_work") if o_work is not None else None,
-                                    _dev(lse_work, "lse_work") if lse_work is not None else None,
+    st = lib().cpattn_ring_attn_fwd(_dev(q, "q"), _dev(k_chunks, "k_chunks", dev) if Skv_c else None,
+                                    _dev(v_chunks, "v_chunks", dev) if Skv_c else None, _dev(o, "o", dev),
+                                    _dev(lse, "lse", dev),
+                                    _dev(o_work, "o_work", dev) if o_work is not None else None,
+                                    _dev(lse_work, "lse_work", dev) if lse_work is not None else None,
                                     B, H, Sq, Skv_c, n, D, float(scale), _stream(stream))
     check("cpattn_ring_attn_fwd", st)
     return o, lse

@@ -145,3 +145,25 @@ def test_rows_are_independent_of_tile_position():
     torch.cuda.synchronize()
     assert torch.equal(o_full[:, :, 512:].view(torch.int16), o_part.view(torch.int16))
     assert torch.equal(l_full[:, :, 512:], l_part)
+
+
+def test_binding_rejects_host_and_strided_operands():
+    """Every pointer the binding hands to the C ABI comes from a contiguous device tensor on q's
+    device: a host or strided K/V (which the library could not tell from a device buffer) is
+    refused before any launch."""
+    q = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros_like(q)
+    host = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16)
+    strided = torch.zeros((1, 2, 128, 128), dtype=torch.bfloat16, device="cuda")[:, :, ::2]
+    for kk, vv in ((host, k), (k, host), (strided, k), (k, strided)):
+        with pytest.raises(ValueError):
+            cp.attn_fwd(q, kk, vv)
+        with pytest.raises(ValueError):
+            cp.attn_fwd_ex(q, kk, vv)
+    q8 = torch.zeros((1, 2, 64, 128), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        cp.attn_fwd_fp8(q8, q8.cpu(), q8)
+    chunks = torch.zeros((2, 1, 2, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        cp.ring_attn_fwd(q, chunks, chunks.cuda())
+    torch.cuda.synchronize()
