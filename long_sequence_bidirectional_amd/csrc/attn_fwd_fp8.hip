@@ -189,7 +189,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
     f32x16 s[NKT];
-    i32x8 pb;                  // P^T bytes: j = 16 kt + i
+    i32x8 pb = {0, 0, 0, 0, 0, 0, 0, 0};   // P^T bytes: j = 16 kt + i
     float m_run = -INFINITY, l_run = 0.f, alpha = 1.f;
 
     // Loads for block j, issued inside M_j: this wave's pieces of K_{j+3} and V_{j+2}, into the
@@ -259,7 +259,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
         alpha = exp2_fast(m_run - m_new);
         m_run = m_new;
         const float mb = kPScaleLog2 - m_new;   // weights come out scaled by 2^7
-        float psum = 0.f;
+        // row sum in four independent partial sums (no serial chain of 32 dependent adds)
+        float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -268,13 +269,14 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     p[e] = exp2_fast(__builtin_fmaf(s[kt][w * 4 + e], c, mb));
-                    psum += p[e];
+                    psum[e] += p[e];
                 }
-                int word = pack_fp8x2<false>(p[0], p[1], 0);
+                // both halves of the word are written, so the previous contents are irrelevant
+                int word = pack_fp8x2<false>(p[0], p[1], pb[kt * 4 + w]);
                 word = pack_fp8x2<true>(p[2], p[3], word);
                 pb[kt * 4 + w] = word;
             }
-        l_run = l_run * alpha + psum;
+        l_run = l_run * alpha + ((psum[0] + psum[1]) + (psum[2] + psum[3]));
         asm volatile("" : "+v"(l_run));
         asm volatile("" : "+v"(pb));
         if (__ballot(raise) != 0) {
