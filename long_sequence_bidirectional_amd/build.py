@@ -38,8 +38,11 @@ def _run(cmd):
     return res.stderr
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every translation unit in parallel, then link the shared library."""
+def build(verbose: bool = False, extra_flags=(), out: str = LIB_PATH) -> str:
+    """Compile every translation unit in parallel, then link the shared library at ``out``.
+
+    ``extra_flags`` go to every compile and to the link (e.g. host-only sanitizer flags
+    for a checking build written somewhere other than the package's library)."""
     from concurrent.futures import ThreadPoolExecutor
 
     t0 = time.time()
@@ -54,17 +57,17 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         workers = min(len(jobs), max(1, min(os.cpu_count() or 1, 16)))
         with ThreadPoolExecutor(max_workers=workers) as pool:
             logs = list(pool.map(lambda j: _run(j[1]), jobs))
-        tmp = LIB_PATH + f".tmp{os.getpid()}"
+        tmp = out + f".tmp{os.getpid()}"
         logs.append(_run([HIPCC, *FLAGS, *extra_flags, "-o", tmp, *[o for o, _ in jobs]]))
-        os.replace(tmp, LIB_PATH)
+        os.replace(tmp, out)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     if verbose:
         noise = [l for log in logs for l in log.splitlines() if "packed-fp32-ops" not in l and l.strip()]
         if noise:
             sys.stderr.write("\n".join(noise) + "\n")
-        print(f"built {LIB_PATH} in {time.time() - t0:.1f}s")
-    return LIB_PATH
+        print(f"built {out} in {time.time() - t0:.1f}s")
+    return out
 
 
 if __name__ == "__main__":

@@ -50,11 +50,22 @@ bool overlap(Range a, Range b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-int64_t dtype_size(cpattn_dtype t) { return t == CPATTN_F32 ? 4 : 2; }
+// A C caller may pass any int in an enum argument, while in C++ a value outside the
+// enumerators' bit range is not a valid value of the enum type.  Entry points therefore
+// read each enum argument's bits as an int, validate that, and only then convert back.
+template <class E>
+int enum_bits(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
+int64_t dtype_size(int t) { return t == CPATTN_F32 ? 4 : 2; }
 bool dtype_valid(int t) { return t == CPATTN_BF16 || t == CPATTN_F32 || t == CPATTN_F16; }
 bool dtype_16bit(int t) { return t == CPATTN_BF16 || t == CPATTN_F16; }
 
-cpattn::MergeOut merge_out(cpattn_dtype t) {
+cpattn::MergeOut merge_out(int t) {
     return t == CPATTN_F32 ? cpattn::MergeOut::F32 : t == CPATTN_F16 ? cpattn::MergeOut::F16 : cpattn::MergeOut::BF16;
 }
 
@@ -212,8 +223,8 @@ struct AttnFwdCheck {
 
 // Checks shared by attn_fwd and attn_fwd_ex (everything but the workspace).
 cpattn_status check_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                             int64_t Sq, int64_t Skv, int64_t D, float scale, cpattn_dtype in_dtype,
-                             cpattn_dtype o_dtype, AttnFwdCheck* out) {
+                             int64_t Sq, int64_t Skv, int64_t D, float scale, int in_dtype, int o_dtype,
+                             AttnFwdCheck* out) {
     if (!q || !o || !lse || (Skv != 0 && (!k || !v))) return CPATTN_E_NULL;
     if (!dtype_valid(in_dtype) || !dtype_valid(o_dtype)) return CPATTN_E_DTYPE;
     if (o_dtype != in_dtype && o_dtype != CPATTN_F32) return CPATTN_E_DTYPE;   // O in the input type or f32
@@ -240,11 +251,12 @@ cpattn_status check_attn_fwd(const void* q, const void* k, const void* v, void* 
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                             int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
                                             cpattn_dtype in_dtype, cpattn_dtype o_dtype, hipStream_t stream) {
+    const int idt = enum_bits(in_dtype), odt = enum_bits(o_dtype);
     AttnFwdCheck ck;
-    const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, &ck);
+    const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, &ck);
     if (st != CPATTN_OK) return st;
-    return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, false, false, nullptr, nullptr, 0,
-                    stream);
+    return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
+                    static_cast<cpattn_dtype>(odt), false, false, nullptr, nullptr, 0, stream);
 }
 
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -255,10 +267,11 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, con
     if ((flags & ~(uint32_t)(CPATTN_FLAG_ACCUMULATE | CPATTN_FLAG_SEQ_MAJOR)) != 0) return CPATTN_E_FLAGS;
     const bool acc = (flags & CPATTN_FLAG_ACCUMULATE) != 0;
     const bool seq_major = (flags & CPATTN_FLAG_SEQ_MAJOR) != 0;
+    const int idt = enum_bits(in_dtype), odt = enum_bits(o_dtype);
     AttnFwdCheck ck;
-    const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, &ck);
+    const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, &ck);
     if (st != CPATTN_OK) return st;
-    if (acc && (!dtype_16bit(in_dtype) || o_dtype != CPATTN_F32)) return CPATTN_E_DTYPE;
+    if (acc && (!dtype_16bit(idt) || odt != CPATTN_F32)) return CPATTN_E_DTYPE;
     // the 16-bit kernels address a 64-row K/V block with 32-bit byte offsets
     if (seq_major && H * D >= (int64_t(1) << 25)) return CPATTN_E_SHAPE;
     if (workspace_bytes != 0 && !workspace) return CPATTN_E_NULL;
@@ -276,8 +289,8 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, con
         ws_o = static_cast<float*>(workspace);
         ws_lse = ws_o + (size_t)ws_pieces * cpattn::kAttnTileRows * D;
     }
-    return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, in_dtype, o_dtype, acc, seq_major, ws_o, ws_lse,
-                    ws_pieces, stream);
+    return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
+                    static_cast<cpattn_dtype>(odt), acc, seq_major, ws_o, ws_lse, ws_pieces, stream);
 }
 
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -287,7 +300,8 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, co
     if ((flags & ~(uint32_t)CPATTN_FLAG_SEQ_MAJOR) != 0) return CPATTN_E_FLAGS;
     const bool seq_major = (flags & CPATTN_FLAG_SEQ_MAJOR) != 0;
     if (!q || !o || !lse || (Skv != 0 && (!k || !v))) return CPATTN_E_NULL;
-    if (o_dtype != CPATTN_BF16 && o_dtype != CPATTN_F32) return CPATTN_E_DTYPE;
+    const int odt = enum_bits(o_dtype);
+    if (odt != CPATTN_BF16 && odt != CPATTN_F32) return CPATTN_E_DTYPE;
     AttnCheck c;
     cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, scale, 32, &c);
     if (st != CPATTN_OK) return st;
@@ -297,7 +311,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, co
         if (!(s > 0.f) || !isfinite(s)) return CPATTN_E_SCALE;
     if (!aligned16(q) || !aligned16(o) || !aligned16(lse) || (Skv && (!aligned16(k) || !aligned16(v))))
         return CPATTN_E_ALIGN;
-    const int64_t osz = dtype_size(o_dtype);
+    const int64_t osz = dtype_size(odt);
     const Range rq = range(q, c.q_elems), rk = range(k, c.kv_elems), rv = range(v, c.kv_elems);
     const Range ro = range(o, c.q_elems * osz), rl = range(lse, c.rows * 4);
     if (overlap(ro, rl) || overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) ||
@@ -322,7 +336,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, co
     a.q_scale = q_scale;
     a.k_scale = k_scale;
     a.v_scale = v_scale;
-    a.out_f32 = o_dtype == CPATTN_F32;
+    a.out_f32 = odt == CPATTN_F32;
     a.stream = stream;
     return hip_status(cpattn::launch_attn_fwd_fp8(a));
 }
@@ -347,13 +361,14 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_workspace_size(int64_t B, int64_t H,
                                                            int64_t D, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
                                                            uint64_t* bytes) {
     if (!bytes) return CPATTN_E_NULL;
-    if (!dtype_valid(in_dtype) || !dtype_valid(o_dtype)) return CPATTN_E_DTYPE;
+    const int idt = enum_bits(in_dtype), odt = enum_bits(o_dtype);
+    if (!dtype_valid(idt) || !dtype_valid(odt)) return CPATTN_E_DTYPE;
     AttnCheck c;
     const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, 1.0f, 32, &c);
     if (st != CPATTN_OK) return st;
     *bytes = 0;
-    if (!dtype_16bit(in_dtype)) return CPATTN_OK;
-    const int64_t slots = device_slots(D, o_dtype == CPATTN_F32);
+    if (!dtype_16bit(idt)) return CPATTN_OK;
+    const int64_t slots = device_slots(D, odt == CPATTN_F32);
     if (slots <= 0) return CPATTN_E_HIP;
     *bytes = plan_split(B * H, Sq, Skv, D, slots, UINT64_MAX).bytes;
     return CPATTN_OK;
@@ -364,9 +379,10 @@ CPATTN_EXPORT cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_
                                               int64_t H, int64_t S, int64_t D, cpattn_dtype o_dtype,
                                               hipStream_t stream) {
     if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return CPATTN_E_NULL;
-    if (!dtype_valid(o_dtype)) return CPATTN_E_DTYPE;
+    const int odt = enum_bits(o_dtype);
+    if (!dtype_valid(odt)) return CPATTN_E_DTYPE;
     if (!dims_ok({B, H, S}, 1)) return CPATTN_E_SHAPE;
-    const int64_t osz = dtype_size(o_dtype);
+    const int64_t osz = dtype_size(odt);
     if (D < 8 || D > 1024 || (D * osz) % 16 != 0) return CPATTN_E_HEADDIM;
     const int64_t rows = prod({B, H, S});
     const int64_t elems = prod({B, H, S, D});
@@ -381,7 +397,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_
     if ((lse_out != lse_a && overlap(lo, la)) || (lse_out != lse_b && overlap(lo, lb))) return CPATTN_E_ALIAS;
     if (overlap(ro, la) || overlap(ro, lb) || overlap(ro, lo) || overlap(lo, ra) || overlap(lo, rb))
         return CPATTN_E_ALIAS;
-    cpattn::MergeArgs m{o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, D, merge_out(o_dtype), stream};
+    cpattn::MergeArgs m{o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, D, merge_out(odt), stream};
     return hip_status(cpattn::launch_attn_merge(m));
 }
 
@@ -428,7 +444,7 @@ CPATTN_EXPORT cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_ch
 namespace {
 
 cpattn_status relayout(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t P,
-                       cpattn_dtype dt, cpattn_dir dir, bool pack, hipStream_t stream) {
+                       int dt, int dir, bool pack, hipStream_t stream) {
     if (!src || !dst) return CPATTN_E_NULL;
     if (!dtype_valid(dt)) return CPATTN_E_DTYPE;
     if (dir != CPATTN_SEQ_TO_HEAD && dir != CPATTN_HEAD_TO_SEQ) return CPATTN_E_SHAPE;
@@ -452,13 +468,13 @@ cpattn_status relayout(const void* src, void* dst, int64_t B, int64_t S_local, i
 CPATTN_EXPORT cpattn_status cpattn_ulysses_pack(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H,
                                                 int64_t D, int64_t P, cpattn_dtype dt, cpattn_dir dir,
                                                 hipStream_t stream) {
-    return relayout(src, dst, B, S_local, H, D, P, dt, dir, true, stream);
+    return relayout(src, dst, B, S_local, H, D, P, enum_bits(dt), enum_bits(dir), true, stream);
 }
 
 CPATTN_EXPORT cpattn_status cpattn_ulysses_unpack(const void* src, void* dst, int64_t B, int64_t S_local,
                                                   int64_t H, int64_t D, int64_t P, cpattn_dtype dt,
                                                   cpattn_dir dir, hipStream_t stream) {
-    return relayout(src, dst, B, S_local, H, D, P, dt, dir, false, stream);
+    return relayout(src, dst, B, S_local, H, D, P, enum_bits(dt), enum_bits(dir), false, stream);
 }
 
 namespace {
@@ -479,7 +495,8 @@ float round_to_bf16_host(float x) {
 CPATTN_EXPORT cpattn_status cpattn_qk_rmsnorm(const void* x, const void* w, void* y, int64_t rows, int64_t D,
                                               float eps, float post_scale, cpattn_dtype dt, hipStream_t stream) {
     if (!x || !w || !y) return CPATTN_E_NULL;
-    if (!dtype_16bit(dt)) return CPATTN_E_DTYPE;
+    const int dtb = enum_bits(dt);
+    if (!dtype_16bit(dtb)) return CPATTN_E_DTYPE;
     if (D < 8 || D > 512 || (D & (D - 1)) != 0) return CPATTN_E_HEADDIM;
     if (rows < 1 || rows > kMaxDim / (D / 8)) return CPATTN_E_SHAPE;   // one thread per 16 bytes
     if (!(eps >= 0.f) || !isfinite(eps) || !(post_scale > 0.f) || !isfinite(post_scale)) return CPATTN_E_SCALE;
@@ -487,7 +504,7 @@ CPATTN_EXPORT cpattn_status cpattn_qk_rmsnorm(const void* x, const void* w, void
     const int64_t bytes = rows * D * 2;
     const Range rx = range(x, bytes), ry = range(y, bytes), rw = range(w, D * 2);
     if ((y != x && overlap(rx, ry)) || overlap(rw, ry)) return CPATTN_E_ALIAS;
-    const bool f16 = dt == CPATTN_F16;
+    const bool f16 = dtb == CPATTN_F16;
     const float s16 = f16 ? round_to_f16_host(post_scale) : round_to_bf16_host(post_scale);
     if (!(s16 > 0.f) || !isfinite(s16)) return CPATTN_E_SCALE;   // underflows or overflows the 16-bit type
     cpattn::QkNormArgs a{x, w, y, rows, D, eps, s16, post_scale != 1.0f, f16, stream};
@@ -495,7 +512,7 @@ CPATTN_EXPORT cpattn_status cpattn_qk_rmsnorm(const void* x, const void* w, void
 }
 
 CPATTN_EXPORT const char* cpattn_status_string(cpattn_status s) {
-    switch (s) {
+    switch (enum_bits(s)) {
         case CPATTN_OK: return "ok";
         case CPATTN_E_NULL: return "a required pointer is NULL";
         case CPATTN_E_SHAPE: return "a size is out of range, inconsistent or overflows";
