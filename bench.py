@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (256 CUs at 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_CLOCK_MHZ = 2400.0     # engine clock the matrix-core peak is quoted at
 LAYERS = 36
 KERNEL_SRC = [os.path.join(ROOT, "long_sequence_bidirectional_amd", "csrc", f)
               for f in ("attn_fwd_kernel.h", "attn_fwd_bf16.hip")]
@@ -136,10 +137,16 @@ def cpu_baseline(budget_s: float):
             t_total += time.perf_counter() - t0
             rows_done += 64
     flops = 4.0 * rows_done * S * D
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(min(cores, blas_threads)),
             "kind": "oracle",
             "sample": f"{rows_done} query rows (blocks of 64) of the S=44160 H=24 D=128 self-attention "
-                      f"over {heads_used} heads, fp64 numpy, {t_total:.1f} s; host has {cores} cores"}
+                      f"over {heads_used} heads, fp64 numpy, {t_total:.1f} s; host has {cores} cores ({cpu})"}
 
 
 def main():
@@ -253,6 +260,9 @@ def main():
                      "min_launch_ms": round(self_sorted[0], 4), "max_launch_ms": round(self_sorted[-1], 4),
                      "socket_power_w": power_clock[0] if power_clock else None,
                      "gfx_clock_mhz": round(power_clock[1]) if power_clock else None,
+                     # the same fraction against the peak scaled to the clock measured during the run
+                     "frac_at_clock": (round(achieved / (PEAK_BF16_TFLOPS * power_clock[1] / PEAK_CLOCK_MHZ), 4)
+                                       if power_clock and power_clock[1] else None),
                      "split": split_of(cp, H, S, S, D, ws_self),
                      "counters": counters},
         "wall_s_timed": round(wall, 3),
