@@ -11,9 +11,11 @@
 // Work split and schedule follow the bf16 kernel: 8 waves, 256 query rows per
 // workgroup, waves w and w+4 on one SIMD alternating an MFMA slot (4 QK + 4 PV MFMAs
 // per 64-key block) with a softmax slot, K/V through four LDS buffers by direct
-// global->LDS loads issued inside the MFMA slot three blocks ahead (the softmax slot,
-// twice as long as the MFMA slot here, is the critical one and issues none), Q^T in
-// registers.
+// global->LDS loads issued inside the MFMA slot three blocks ahead, Q^T in registers.
+// The softmax slot is the critical one here (its exponentials, at one wave's VALU
+// issue rate, outlast the MFMA slot, whose length is set by the 16 KB of LDS operands
+// a wave reads per block), so it issues no loads and the MFMA slot takes over the row
+// max of the block it has just multiplied, between its PV MFMAs.
 //
 // Operand layouts of the 32x32x64 fp8 MFMA: lane (row/column l%32, half h = l/32)
 // holds 32 bytes of its row of A (column of B); byte j of half h of A meets byte j
@@ -201,10 +203,49 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     auto issue_v = [&]<int R>(ic<R>, int j) CPATTN_AI {
         if (j + 2 < nblk) load_block(vp, Vs[(R + 2) % 4], j + 2, false);
     };
-    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1); R = j % 4
+    // Row max of S_j (keys past Skv in the last block first set to -inf), in two halves so
+    // that each follows a PV MFMA, then the lazy raise of the running max and alpha.
+    float mx_part = -INFINITY;
+    bool raise = false;
+    auto row_max_half = [&](int kt, int j) CPATTN_AI {
+        if (kt == 0 && j == nblk - 1 && (Skv % BN) != 0) {
+#pragma unroll
+            for (int t = 0; t < NKT; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = j * BN + swap23(t * 32 + (i >> 2) * 8 + hh * 4 + (i & 3));
+                    if (key >= Skv) s[t][i] = -INFINITY;
+                }
+        }
+        float mx = kt == 0 ? s[0][0] : mx_part;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+        mx_part = mx;
+    };
+    auto raise_max = [&]() CPATTN_AI {
+        const float mx = max_across_halves(mx_part) * c;
+        raise = mx > m_run + kRaiseTh;
+        const float m_new = raise ? mx : m_run;
+        alpha = exp2_fast(m_run - m_new);
+        m_run = m_new;
+    };
+    // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1), then the row max of
+    // S_j; R = j % 4.  Every operand of the slot is read from LDS up front, so no MFMA waits
+    // on a read issued just before it.
     auto M = [&]<int R, bool QK, bool PV>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>, int j) CPATTN_AI {
         constexpr int KB = R, VB = (R + 3) % 4;
         __builtin_amdgcn_s_setprio(1);
+        i32x8 kf[NKS * NKT], vf[NDT];
+        if constexpr (QK) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) kf[ks * NKT + kt] = read_k(ic<KB>{}, kt, ks);
+        }
+        if constexpr (PV) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) vf[dt] = read_vt(ic<VB>{}, dt);
+        }
         if constexpr (QK) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
@@ -214,7 +255,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
             for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt) {
-                    s[kt] = mfma8(read_k(ic<KB>{}, kt, ks), qreg[ks], s[kt]);
+                    s[kt] = mfma8(kf[ks * NKT + kt], qreg[ks], s[kt]);
                     if (ks == 0 && kt == 1) {
                         __builtin_amdgcn_sched_barrier(0);
                         issue_k(ic<R>{}, j);
@@ -222,43 +263,38 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
                     }
                 }
         }
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (PV) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                oacc[dt] = mfma8(read_vt(ic<VB>{}, dt), pb, oacc[dt]);
-                if (dt == 1 && QK) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue_v(ic<R>{}, j);
+                oacc[dt] = mfma8(vf[dt], pb, oacc[dt]);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (QK) {
+                    if (dt == 0) row_max_half(0, j);
+                    if (dt == 1) {
+                        issue_v(ic<R>{}, j);
+                        __builtin_amdgcn_sched_barrier(0);
+                        row_max_half(1, j);
+                        raise_max();
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         } else if constexpr (QK) {
             issue_v(ic<R>{}, j);
+            row_max_half(0, j);
+            row_max_half(1, j);
+            raise_max();
         }
         __builtin_amdgcn_s_setprio(0);
     };
-    // SM_j: softmax of S_j -> P_j (E4M3 of p * 2^7), row statistics, O *= alpha when raised
-    auto SM = [&](int j) CPATTN_AI {
-        if (j == nblk - 1 && (Skv % BN) != 0) {
-#pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j * BN + swap23(kt * 32 + (i >> 2) * 8 + hh * 4 + (i & 3));
-                    if (key >= Skv) s[kt][i] = -INFINITY;
-                }
-        }
-        float mx = s[0][0];
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-        mx = max_across_halves(mx) * c;
-        const bool raise = mx > m_run + kRaiseTh;
-        const float m_new = raise ? mx : m_run;
-        alpha = exp2_fast(m_run - m_new);
-        m_run = m_new;
-        const float mb = kPScaleLog2 - m_new;   // weights come out scaled by 2^7
+    // SM_j: P_j (E4M3 of p * 2^7) from S_j and the running max, the row sum, O *= alpha when
+    // some row raised its max
+    auto SM = [&]() CPATTN_AI {
+        // every weight reads m_run: tying it here keeps this work after the slot barrier
+        // (the barrier orders memory only, and the max is already known before it)
+        asm volatile("" : "+v"(m_run));
+        const float mb = kPScaleLog2 - m_run;   // weights come out scaled by 2^7
         // row sum in four independent partial sums (no serial chain of 32 dependent adds)
         float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -310,7 +346,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
         wait_older(j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
-        if constexpr (QK) SM(j);
+        if constexpr (QK) SM();
         wait_older(j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
