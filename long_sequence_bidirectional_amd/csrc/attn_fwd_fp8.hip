@@ -197,18 +197,31 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     // Loads for block j, issued inside M_j: this wave's pieces of K_{j+3} and V_{j+2}, into the
     // buffers of K_{j-1} and V_{j-2}, which M_{j-1} of both groups finished reading before the
     // previous barrier.  The softmax slot, the critical one here, issues none.
-    auto issue_k = [&]<int R>(ic<R>, int j) CPATTN_AI {
-        if (j + 3 < nblk) load_block(kp, Ks[(R + 3) % 4], j + 3, true);
+    // FULL: the caller guarantees K_{j+3} and V_{j+2} exist and are full blocks (no runtime
+    // check, so no branch in the MFMA stream)
+    auto dma_full = [&](const uint8_t* src, uint8_t* dst, int j, uint32_t off) CPATTN_AI {
+        const uint32_t lds = (uint32_t)(uintptr_t)LDS_PTR(void, dst + wave_u * 1024);
+        const uint8_t* blk = src + (int64_t)j * BN * kv_row;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:0"
+                     :: "v"(off), "s"(blk), "s"(lds) : "memory", "m0");
+#pragma clang diagnostic pop
     };
-    auto issue_v = [&]<int R>(ic<R>, int j) CPATTN_AI {
-        if (j + 2 < nblk) load_block(vp, Vs[(R + 2) % 4], j + 2, false);
+    auto issue_k = [&]<int R, bool FULL>(ic<R>, std::bool_constant<FULL>, int j) CPATTN_AI {
+        if constexpr (FULL) dma_full(kp, Ks[(R + 3) % 4], j + 3, koffb);
+        else if (j + 3 < nblk) load_block(kp, Ks[(R + 3) % 4], j + 3, true);
+    };
+    auto issue_v = [&]<int R, bool FULL>(ic<R>, std::bool_constant<FULL>, int j) CPATTN_AI {
+        if constexpr (FULL) dma_full(vp, Vs[(R + 2) % 4], j + 2, voffb);
+        else if (j + 2 < nblk) load_block(vp, Vs[(R + 2) % 4], j + 2, false);
     };
     // Row max of S_j (keys past Skv in the last block first set to -inf), in two halves so
     // that each follows a PV MFMA, then the lazy raise of the running max and alpha.
     float mx_part = -INFINITY;
     bool raise = false;
-    auto row_max_half = [&](int kt, int j) CPATTN_AI {
-        if (kt == 0 && j == nblk - 1 && (Skv % BN) != 0) {
+    auto row_max_half = [&]<bool FULL>(int kt, std::bool_constant<FULL>, int j) CPATTN_AI {
+        if (!FULL && kt == 0 && j == nblk - 1 && (Skv % BN) != 0) {
 #pragma unroll
             for (int t = 0; t < NKT; ++t)
 #pragma unroll
@@ -232,7 +245,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1), then the row max of
     // S_j; R = j % 4.  Every operand of the slot is read from LDS up front, so no MFMA waits
     // on a read issued just before it.
-    auto M = [&]<int R, bool QK, bool PV>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>, int j) CPATTN_AI {
+    auto M = [&]<int R, bool QK, bool PV, bool FULL>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>,
+                                                   std::bool_constant<FULL>, int j) CPATTN_AI {
         constexpr int KB = R, VB = (R + 3) % 4;
         __builtin_amdgcn_s_setprio(1);
         i32x8 kf[NKS * NKT], vf[NDT];
@@ -258,7 +272,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
                     s[kt] = mfma8(kf[ks * NKT + kt], qreg[ks], s[kt]);
                     if (ks == 0 && kt == 1) {
                         __builtin_amdgcn_sched_barrier(0);
-                        issue_k(ic<R>{}, j);
+                        issue_k(ic<R>{}, std::bool_constant<FULL>{}, j);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -270,20 +284,20 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
                 oacc[dt] = mfma8(vf[dt], pb, oacc[dt]);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (QK) {
-                    if (dt == 0) row_max_half(0, j);
+                    if (dt == 0) row_max_half(0, std::bool_constant<FULL>{}, j);
                     if (dt == 1) {
-                        issue_v(ic<R>{}, j);
+                        issue_v(ic<R>{}, std::bool_constant<FULL>{}, j);
                         __builtin_amdgcn_sched_barrier(0);
-                        row_max_half(1, j);
+                        row_max_half(1, std::bool_constant<FULL>{}, j);
                         raise_max();
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         } else if constexpr (QK) {
-            issue_v(ic<R>{}, j);
-            row_max_half(0, j);
-            row_max_half(1, j);
+            issue_v(ic<R>{}, std::bool_constant<FULL>{}, j);
+            row_max_half(0, std::bool_constant<FULL>{}, j);
+            row_max_half(1, std::bool_constant<FULL>{}, j);
             raise_max();
         }
         __builtin_amdgcn_s_setprio(0);
@@ -324,8 +338,8 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     };
     // wait until at most this wave's latest issue (two loads when full) is in flight: then
     // the blocks issued in M_{j-2} are complete before the barrier ahead of slot 2j+1
-    auto wait_older = [&](int jl) CPATTN_AI {
-        if (jl + 3 < nblk) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    auto wait_older = [&]<bool FULL>(std::bool_constant<FULL>, int jl) CPATTN_AI {
+        if (FULL || jl + 3 < nblk) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
@@ -340,14 +354,15 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     // Both groups run M_0, SM_0, ..., M_nblk; group 1 one slot behind (an extra barrier up
     // front; group 0 adds one at the end).
     auto slot_barrier = [&]() CPATTN_AI { asm volatile("s_barrier" ::: "memory"); };
-    auto body = [&]<int R, bool QK, bool PV>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>, int j) CPATTN_AI {
-        M(ic<R>{}, std::bool_constant<QK>{}, std::bool_constant<PV>{}, j);
+    auto body = [&]<int R, bool QK, bool PV, bool FULL = false>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>,
+                                                              int j, std::bool_constant<FULL> = {}) CPATTN_AI {
+        M(ic<R>{}, std::bool_constant<QK>{}, std::bool_constant<PV>{}, std::bool_constant<FULL>{}, j);
         __builtin_amdgcn_sched_barrier(0);
-        wait_older(j);
+        wait_older(std::bool_constant<FULL>{}, j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
         if constexpr (QK) SM();
-        wait_older(j);
+        wait_older(std::bool_constant<FULL>{}, j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
     };
@@ -356,6 +371,15 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     if (group != 0) slot_barrier();
     body(ic<0>{}, T{}, F{}, 0);
     int j = 1;
+    // steady state with no runtime checks: every load of these four blocks is a full block
+    // and none of them is the last block (each check removed is a branch in the slots)
+    const int nfull = Skv / BN;
+    for (; j + 7 <= nfull; j += 4) {
+        body(ic<1>{}, T{}, T{}, j, T{});
+        body(ic<2>{}, T{}, T{}, j + 1, T{});
+        body(ic<3>{}, T{}, T{}, j + 2, T{});
+        body(ic<0>{}, T{}, T{}, j + 3, T{});
+    }
     for (; j + 3 < nblk; j += 4) {
         body(ic<1>{}, T{}, T{}, j);
         body(ic<2>{}, T{}, T{}, j + 1);

@@ -340,21 +340,35 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     // NP_M pieces go between the MFMAs of M_j, the last one at the end of SM_j, where the
     // softmax wave would otherwise wait at the barrier.
     constexpr int NP_M = 2 * LOADS_PER_WAVE - 1;
-    auto issue_part = [&]<int R, int P>(ic<R>, ic<P>, int j) CPATTN_AI {
+    // FULL: the caller guarantees that K_{j+3} and V_{j+2} exist and are full blocks, so the
+    // piece goes out with no runtime check (no branch in the MFMA stream).
+    auto issue_part = [&]<int R, int P, bool FULL>(ic<R>, ic<P>, std::bool_constant<FULL>, int j) CPATTN_AI {
         if constexpr (P < LOADS_PER_WAVE) {
-            if (j + 3 < nblk) load_piece(ic<P>{}, kp, Ks[(R + 3) % 4], j + 3, false);
+            if constexpr (FULL) {
+                dma(ic<P>{}, koffb[P], reinterpret_cast<const char*>(kp + (int64_t)(j + 3) * BN * kv_row),
+                    (uint32_t)(uintptr_t)LDS_PTR(void, Ks[(R + 3) % 4] + wave_u * LOADS_PER_WAVE * 512));
+            } else {
+                if (j + 3 < nblk) load_piece(ic<P>{}, kp, Ks[(R + 3) % 4], j + 3, false);
+            }
         } else {
-            if (j + 2 < nblk) load_piece(ic<P - LOADS_PER_WAVE>{}, vp, Vs[(R + 2) % 4], j + 2, true);
+            constexpr int Q = P - LOADS_PER_WAVE;
+            if constexpr (FULL) {
+                dma(ic<Q>{}, voffb[Q], reinterpret_cast<const char*>(vp + (int64_t)(j + 2) * BN * kv_row),
+                    (uint32_t)(uintptr_t)LDS_PTR(void, Vs[(R + 2) % 4] + wave_u * LOADS_PER_WAVE * 512));
+            } else {
+                if (j + 2 < nblk) load_piece(ic<Q>{}, vp, Vs[(R + 2) % 4], j + 2, true);
+            }
         }
     };
     // M_j: S_j = K_j Q^T (j < nblk) and O += V_{j-1} P_{j-1} (j >= 1); R = j % 4.
-    auto M = [&]<int R, bool QK, bool PV, bool USE_PRE>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>,
-                                                      std::bool_constant<USE_PRE>, int j) CPATTN_AI {
+    auto M = [&]<int R, bool QK, bool PV, bool USE_PRE, bool FULL>(ic<R>, std::bool_constant<QK>,
+                                                                 std::bool_constant<PV>, std::bool_constant<USE_PRE>,
+                                                                 std::bool_constant<FULL>, int j) CPATTN_AI {
         constexpr int KB = R, VB = (R + 3) % 4;
         auto hook = [&]<int I, int NJ>(ic<I>, ic<NJ>) CPATTN_AI {
             constexpr int GAP = NJ / NP_M;
             if constexpr (I % GAP == GAP / 2 && I / GAP < NP_M) {
-                issue_part(ic<R>{}, ic<I / GAP>{}, j);
+                issue_part(ic<R>{}, ic<I / GAP>{}, std::bool_constant<FULL>{}, j);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -363,14 +377,15 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
         __builtin_amdgcn_s_setprio(0);
     };
     // SM_j: softmax of S_j -> P_j, row statistics, O *= alpha_j when some row raised its max.
-    auto SM = [&]<int R>(ic<R>, int j) CPATTN_AI {
+    // FULL: block j+1 exists and block j is not the last one.
+    auto SM = [&]<int R, bool FULL>(ic<R>, std::bool_constant<FULL>, int j) CPATTN_AI {
         if constexpr (NPF > 0) {
-            if (j + 1 < nblk) {
+            if (FULL || j + 1 < nblk) {
 #pragma unroll
                 for (int i = 0; i < NPF; ++i) pre[i] = read_k(ic<(R + 1) % 4>{}, i % NKT, i / NKT);
             }
         }
-        if (j == nblk - 1 && (Skv % BN) != 0) {
+        if (!FULL && j == nblk - 1 && (Skv % BN) != 0) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -418,9 +433,9 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     };
     // Wait until at most this wave's latest issue of loads (made in M_jl) is in flight: exact
     // while that issue was a full one (K and V); near the end, where issues carry fewer loads,
-    // wait for everything.
-    auto wait_older = [&](int jl) CPATTN_AI {
-        if (jl + 3 < nblk)
+    // wait for everything.  FULL: that issue was a full one.
+    auto wait_older = [&]<bool FULL>(std::bool_constant<FULL>, int jl) CPATTN_AI {
+        if (FULL || jl + 3 < nblk)
             asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS_PER_WAVE) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -443,19 +458,21 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     // are in LDS by the start of slot 2j+1: SM_j prefetches K_{j+1} fragments from there,
     // and M_{j+1} reads K_{j+1}, V_j.  The slot barrier itself does not wait for memory.
     auto slot_barrier = [&]() CPATTN_AI { asm volatile("s_barrier" ::: "memory"); };
-    auto body = [&]<int R, bool QK, bool PV, bool USE_PRE>(ic<R>, std::bool_constant<QK>, std::bool_constant<PV>,
-                                                         std::bool_constant<USE_PRE>, int j) CPATTN_AI {
-        M(ic<R>{}, std::bool_constant<QK>{}, std::bool_constant<PV>{}, std::bool_constant<USE_PRE>{}, j);
+    auto body = [&]<int R, bool QK, bool PV, bool USE_PRE, bool FULL = false>(
+                    ic<R>, std::bool_constant<QK>, std::bool_constant<PV>, std::bool_constant<USE_PRE>, int j,
+                    std::bool_constant<FULL> = {}) CPATTN_AI {
+        M(ic<R>{}, std::bool_constant<QK>{}, std::bool_constant<PV>{}, std::bool_constant<USE_PRE>{},
+          std::bool_constant<FULL>{}, j);
         __builtin_amdgcn_sched_barrier(0);
-        wait_older(j);
+        wait_older(std::bool_constant<FULL>{}, j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
         if constexpr (QK) {
-            SM(ic<R>{}, j);
+            SM(ic<R>{}, std::bool_constant<FULL>{}, j);
             __builtin_amdgcn_sched_barrier(0);
-            issue_part(ic<R>{}, ic<NP_M>{}, j);
+            issue_part(ic<R>{}, ic<NP_M>{}, std::bool_constant<FULL>{}, j);
         }
-        wait_older(j);
+        wait_older(std::bool_constant<FULL>{}, j);
         __builtin_amdgcn_sched_barrier(0);
         slot_barrier();
     };
@@ -464,6 +481,17 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     if (group != 0) slot_barrier();
     body(ic<0>{}, T{}, F{}, F{}, 0);
     int j = 1;
+    // Steady state, with no runtime checks: every load these four blocks issue (K up to
+    // block j+6, V up to j+5) is a full block, and none of them is the last block.  Each
+    // check removed is a scalar branch in the MFMA or softmax stream; taken branches there
+    // cost the schedule far more than their instructions (measured: 5% of the kernel).
+    const int nfull = Skv / BN;
+    for (; j + 7 <= nfull; j += 4) {
+        body(ic<1>{}, T{}, T{}, T{}, j, T{});
+        body(ic<2>{}, T{}, T{}, T{}, j + 1, T{});
+        body(ic<3>{}, T{}, T{}, T{}, j + 2, T{});
+        body(ic<0>{}, T{}, T{}, T{}, j + 3, T{});
+    }
     for (; j + 3 < nblk; j += 4) {
         body(ic<1>{}, T{}, T{}, T{}, j);
         body(ic<2>{}, T{}, T{}, T{}, j + 1);
