@@ -424,7 +424,7 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
         asm volatile("" : "+v"(l_run));
 #pragma unroll
         for (int t = 0; t < NPB; ++t) asm volatile("" : "+v"(pb[t]));
-        if (__ballot(raise) != 0) {
+        if (__builtin_expect(__ballot(raise) != 0, 0)) {   // rare: keep the common path free of taken branches
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
