@@ -6,8 +6,10 @@ the loads three blocks ahead, a remainder runs the last one to three blocks of
 the unrolled loop, and a final slot does the last PV product alone.  Key counts
 1..6 blocks (and one key either side of each block edge) exercise every such
 path, in the bf16, fp16 and fp8 kernels, with and without a ragged query tile;
-the split path is checked with pieces of four to five blocks.  Oracle: exact
-fp64 attention of the same inputs; bounds as in the other parity tests.
+the split path is checked with pieces of four to five blocks, and key counts of
+7..13 blocks cover the entry into and exit from the check-free steady-state
+loop.  Oracle: exact fp64 attention of the same inputs; bounds as in the other
+parity tests.
 """
 import math
 
@@ -87,3 +89,36 @@ def test_split_short_pieces(Skv):
     torch.cuda.synchronize()
     O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
     assert_bf16_parity(host64(o), host64(lse), O, L, f"split Skv={Skv}")
+
+
+# Key counts around the start of the check-free steady-state loop: it runs while every load of
+# its four blocks is a full block (full blocks >= j + 7 for j = 1, 5, ...), then the checked
+# loop, the remainder and the final slot take over; 7..13 blocks, full or with a ragged tail.
+STEADY = [448, 449, 511, 512, 513, 575, 576, 577, 640, 641, 703, 704, 705, 767, 768, 769, 831, 832, 833]
+
+
+@pytest.mark.parametrize("Skv", STEADY)
+def test_bf16_steady_state_entry(Skv):
+    B, H, Sq, D = 1, 2, 300, 128
+    log(f"case: bf16 steady-state entry B{B} H{H} Sq{Sq} Skv{Skv} D{D}")
+    seed = 8400 + Skv
+    qb = inputs.random_bf16((B, H, Sq, D), seed)
+    kb = inputs.random_bf16((B, H, Skv, D), seed + 1)
+    vb = inputs.random_bf16((B, H, Skv, D), seed + 2)
+    o, lse = cp.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb))
+    torch.cuda.synchronize()
+    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+    assert_bf16_parity(host64(o), host64(lse), O, L, f"bf16 Skv={Skv}")
+
+
+@pytest.mark.parametrize("Skv", STEADY[::2])
+def test_fp8_steady_state_entry(Skv):
+    B, H, Sq, D = 1, 2, 300, 128
+    log(f"case: fp8 steady-state entry B{B} H{H} Sq{Sq} Skv{Skv} D{D}")
+    seed = 8500 + Skv
+    q8 = inputs.random_e4m3((B, H, Sq, D), seed)
+    k8 = inputs.random_e4m3((B, H, Skv, D), seed + 1)
+    v8 = inputs.random_e4m3((B, H, Skv, D), seed + 2)
+    o, lse = cp.attn_fwd_fp8(dev8(q8), dev8(k8), dev8(v8))
+    torch.cuda.synchronize()
+    check_fp8(q8, k8, v8, 1.0, 1.0, 1.0, 1.0 / math.sqrt(D), o, lse, f"fp8 Skv={Skv}")
