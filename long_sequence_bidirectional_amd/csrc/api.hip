@@ -201,11 +201,12 @@ cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, flo
     a.accumulate = accumulate;
     a.split_tiles = 0;
     a.split_pieces = 1;
+    a.slots = 0;
     a.stream = stream;
     if (in_dtype == CPATTN_F32) return hip_status(cpattn::launch_attn_fwd_f32(a));
+    a.slots = device_slots(D, a.out_f32);
     if (ws_o && ws_lse && ws_pieces > 0) {
-        const SplitPlan p = plan_split(BH, Sq, Skv, D, device_slots(D, a.out_f32),
-                                       (uint64_t)ws_pieces * piece_bytes(D));
+        const SplitPlan p = plan_split(BH, Sq, Skv, D, a.slots, (uint64_t)ws_pieces * piece_bytes(D));
         if (p.split_tiles > 0) {
             a.split_tiles = p.split_tiles;
             a.split_pieces = p.pieces;

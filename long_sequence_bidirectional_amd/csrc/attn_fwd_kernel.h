@@ -127,9 +127,10 @@ __device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
     else return pack_bf16x2(lo, hi);
 }
 
+// One work unit (a whole tile or a key-range piece of one) of a workgroup.
 template <int D, bool F16, bool OUT_F32, bool SEQ>
-__global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+__device__ __forceinline__ void attn_unit(
+    int bid, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
     Strides so, AttnTileMap map, float c) {
     constexpr int BN = kBN;
@@ -156,7 +157,6 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     // that neighbours read the same keys.  A piece p of s covers key blocks
     // [p*nblk/s, (p+1)*nblk/s) and leaves a normalised f32 partial and its LSE
     // in workspace slot (tile - n_dp) * s + p.
-    const int bid = blockIdx.x;
     const int nblk_all = (Skv_all + BN - 1) / BN;
     int tile, kb0 = 0, slot = -1, nblk = nblk_all;
     if (bid < map.grid_dp) {
@@ -562,6 +562,20 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     }
 }
 
+// At most one workgroup per resident slot, each looping over work units u = blockIdx.x +
+// k * gridDim.x: a finished unit is followed by the next one without a new workgroup launch.
+// gridDim.x is a multiple of the XCD count, so unit u still runs on XCD u % 8, which the unit
+// order above relies on.  A unit's last LDS reads end before its final barrier, so the next
+// unit's loads into the same buffers need no extra synchronisation.
+template <int D, bool F16, bool OUT_F32, bool SEQ>
+__global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
+    Strides so, AttnTileMap map, float c, int n_units) {
+    for (int u = blockIdx.x; u < n_units; u += gridDim.x)
+        attn_unit<D, F16, OUT_F32, SEQ>(u, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv, so, map, c);
+}
+
 template <int D, bool F16, bool OUT_F32, bool SEQ>
 hipError_t launch(const AttnFwdArgs& a) {
     const int nQt = (int)((a.Sq + kBM - 1) / kBM);
@@ -576,12 +590,14 @@ hipError_t launch(const AttnFwdArgs& a) {
     m.ws_o = a.ws_o;
     m.ws_lse = a.ws_lse;
     m.accumulate = a.accumulate ? 1 : 0;
-    const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;
+    const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;   // work units (a multiple of kNumXcd)
     const float c = (float)((double)a.scale * 1.4426950408889634);
-    hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, F16, OUT_F32, SEQ>), dim3(grid), dim3(512), 0, a.stream,
+    const int64_t cap = a.slots - a.slots % kNumXcd;
+    const int launch_grid = (cap > 0 && grid > cap) ? (int)cap : grid;
+    hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, F16, OUT_F32, SEQ>), dim3(launch_grid), dim3(512), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)a.H, a.sq,
-                       a.skv, a.so, m, c);
+                       a.skv, a.so, m, c, grid);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_tiles == 0) return e;
     MergePiecesArgs f{a.ws_o, a.ws_lse, a.o, a.lse, m.n_dp, m.n_split, m.split_s, nQt, a.H, a.so, a.Sq, a.D,

@@ -41,6 +41,9 @@ struct AttnFwdArgs {
     int64_t split_pieces;
     float* ws_o;
     float* ws_lse;
+    // Workgroups of the 16-bit kernel resident at once on the current device (0 = unknown):
+    // the kernel is launched with at most that many workgroups, each looping over work units.
+    int64_t slots;
     hipStream_t stream;
 };
 
