@@ -61,7 +61,13 @@
 //    otherwise wait at the barrier; loads run three blocks ahead of use (four
 //    buffers).
 // Slot barriers are plain s_barrier: each wave waits only for its own older
-// loads (vmcnt) before arriving.
+// loads (vmcnt) before arriving.  The steady state of the block loop carries no
+// runtime checks (it runs while every load of its four blocks is a full block):
+// a per-block check costs a compare and, in the common case, a taken scalar
+// branch in the MFMA or softmax stream, which the schedule pays far above its
+// instruction count.  Workgroups are persistent: at most one per resident slot,
+// each looping over work units, so a finished unit is followed by the next one
+// without a new workgroup launch.
 //
 // Softmax in base 2: t = s * scale * log2(e), p = exp2(t - m), natural
 // LSE = (m + log2 l) * ln 2.  The running max m is only raised when a block's
@@ -572,8 +578,8 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
     Strides so, AttnTileMap map, float c, int n_units) {
-    for (int u = blockIdx.x; u < n_units; u += gridDim.x)
-        attn_unit<D, F16, OUT_F32, SEQ>(u, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv, so, map, c);
+    for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x)   // 64-bit: no overflow near INT_MAX units
+        attn_unit<D, F16, OUT_F32, SEQ>((int)u, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv, so, map, c);
 }
 
 template <int D, bool F16, bool OUT_F32, bool SEQ>
