@@ -9,10 +9,11 @@
 // O = 0, LSE = -inf.
 //
 // HBM-bound: per row it reads 2*D values of O and two LSEs and writes D + 1.
-// Each row is handled inside one wave (lanes = 8-element chunks of the row),
-// so an in-place call (o_out == o_a, lse_out == lse_a) is safe: every lane of
-// the row loads both LSEs in the same instruction, before the one lane that
-// writes lse_out, and each lane rewrites only the O chunk it read itself.
+// A row of O is D*sizeof(O)/16 16-byte vectors (the entry point requires a
+// whole number of them).  Each row is handled inside one wave, one vector per
+// lane, so an in-place call (o_out == o_a, lse_out == lse_a) is safe: every
+// lane of the row loads both LSEs in the same instruction, before the one lane
+// that writes lse_out, and each lane rewrites only the vectors it read itself.
 #include "common.h"
 #include "kernels.h"
 
@@ -51,35 +52,49 @@ __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, flo
     }
 }
 
-// Fast path (D/8 <= 64): each wave owns MU groups of 64/(D/8) rows; every lane loads all of
-// its chunks (both operands, both LSEs) before computing and storing any of them.
+// One 16-byte vector of a row: 4 f32 or 8 16-bit values of O.
+template <MergeOut T>
+__device__ __forceinline__ u32x4 merge_vec(const u32x4& a, const u32x4& b, float wa, float wb) {
+    if constexpr (T == MergeOut::F32) {
+        const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+        return __builtin_bit_cast(u32x4, x * wa + y * wb);
+    } else {
+        u32x4 r;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            r[w] = pack16<T>(__builtin_fmaf(lo16<T>(a[w]), wa, lo16<T>(b[w]) * wb),
+                             __builtin_fmaf(hi16<T>(a[w]), wa, hi16<T>(b[w]) * wb));
+        return r;
+    }
+}
+
+// Fast path (a row of vr <= 64 16-byte vectors): a wave owns MU groups of rpw = 64 / vr
+// consecutive rows, one vector per lane and group, so each load or store instruction covers
+// rpw whole rows of O contiguously.  Every lane loads all of its vectors (both operands, both
+// LSEs) before computing and storing any of them.
 template <MergeOut T, int MU>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const void* o_a, const float* lse_a, const void* o_b,
                                                          const float* lse_b, void* o_out, float* lse_out,
-                                                         int64_t rows, int D, int rows_per_wave) {
+                                                         int64_t rows, int vr, int rpw) {
     const int lane = threadIdx.x & 63;
     const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int tpr = D >> 3;
-    const int r_in = lane / tpr;
-    if (r_in >= rows_per_wave) return;
-    const int ch = lane - r_in * tpr;
-    constexpr bool F32 = T == MergeOut::F32;
-    constexpr int NV = F32 ? 2 : 1;     // 16-byte vectors per 8-element chunk
-    u32x4 a[MU][NV], b[MU][NV];
+    const int r_in = lane / vr;
+    if (r_in >= rpw) return;
+    const int vec = lane - r_in * vr;
+    const u32x4* pa = static_cast<const u32x4*>(o_a);
+    const u32x4* pb = static_cast<const u32x4*>(o_b);
+    u32x4 a[MU], b[MU];
     float la[MU], lb[MU];
     int64_t row[MU];
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
-        row[u] = (gwave * MU + u) * rows_per_wave + r_in;
+        row[u] = (gwave * MU + u) * rpw + r_in;
         if (row[u] < rows) {
             la[u] = lse_a[row[u]];
             lb[u] = lse_b[row[u]];
-            const size_t off = ((size_t)row[u] * D + (size_t)ch * 8) * (F32 ? 4 : 2) / 16;
-#pragma unroll
-            for (int w = 0; w < NV; ++w) {
-                a[u][w] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o_a) + off + w);
-                b[u][w] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o_b) + off + w);
-            }
+            const size_t off = (size_t)row[u] * vr + vec;
+            a[u] = __builtin_nontemporal_load(pa + off);
+            b[u] = __builtin_nontemporal_load(pb + off);
         }
     }
 #pragma unroll
@@ -87,62 +102,32 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* o_a, const 
         if (row[u] >= rows) continue;
         float wa, wb, L;
         merge_weights(la[u], lb[u], wa, wb, L);
-        const size_t off = ((size_t)row[u] * D + (size_t)ch * 8) * (F32 ? 4 : 2) / 16;
-        if constexpr (F32) {
-#pragma unroll
-            for (int w = 0; w < NV; ++w) {
-                const f32x4 x = __builtin_bit_cast(f32x4, a[u][w]), y = __builtin_bit_cast(f32x4, b[u][w]);
-                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x * wa + y * wb),
-                                            reinterpret_cast<u32x4*>(o_out) + off + w);
-            }
-        } else {
-            u32x4 r;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float alo = lo16<T>(a[u][0][w]), ahi = hi16<T>(a[u][0][w]);
-                const float blo = lo16<T>(b[u][0][w]), bhi = hi16<T>(b[u][0][w]);
-                r[w] = pack16<T>(__builtin_fmaf(alo, wa, blo * wb), __builtin_fmaf(ahi, wa, bhi * wb));
-            }
-            __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(o_out) + off);
-        }
-        if (ch == 0) lse_out[row[u]] = L;
+        __builtin_nontemporal_store(merge_vec<T>(a[u], b[u], wa, wb),
+                                    static_cast<u32x4*>(o_out) + (size_t)row[u] * vr + vec);
+        if (vec == 0) lse_out[row[u]] = L;
     }
 }
 
-// General path (D/8 > 64): one row per wave, lanes loop over the row's chunks.
+// General path (vr > 64): one row per wave, lanes loop over the row's vectors, two at a time.
 template <MergeOut T>
 __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const void* o_a, const float* lse_a, const void* o_b,
                                                               const float* lse_b, void* o_out, float* lse_out,
-                                                              int64_t rows, int D) {
+                                                              int64_t rows, int vr) {
     const int lane = threadIdx.x & 63;
     const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     if (row >= rows) return;
-    constexpr bool F32 = T == MergeOut::F32;
     float wa, wb, L;
     merge_weights(lse_a[row], lse_b[row], wa, wb, L);
-    const int tpr = D >> 3;
-    for (int ch = lane; ch < tpr; ch += 64) {
-        const size_t off = (size_t)row * D + (size_t)ch * 8;
-        if constexpr (F32) {
-            const f32x4* pa = reinterpret_cast<const f32x4*>(static_cast<const float*>(o_a) + off);
-            const f32x4* pb = reinterpret_cast<const f32x4*>(static_cast<const float*>(o_b) + off);
-            const f32x4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
-            f32x4* po = reinterpret_cast<f32x4*>(static_cast<float*>(o_out) + off);
-            po[0] = a0 * wa + b0 * wb;
-            po[1] = a1 * wa + b1 * wb;
-        } else {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o_a) + off);
-            const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(o_b) + off);
-            u32x4 r;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float alo = lo16<T>(a[w]), ahi = hi16<T>(a[w]);
-                const float blo = lo16<T>(b[w]), bhi = hi16<T>(b[w]);
-                r[w] = pack16<T>(__builtin_fmaf(alo, wa, blo * wb), __builtin_fmaf(ahi, wa, bhi * wb));
-            }
-            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(o_out) + off) = r;
-        }
+    const u32x4* pa = static_cast<const u32x4*>(o_a) + (size_t)row * vr;
+    const u32x4* pb = static_cast<const u32x4*>(o_b) + (size_t)row * vr;
+    u32x4* po = static_cast<u32x4*>(o_out) + (size_t)row * vr;
+    int v = lane;
+    for (; v + 64 < vr; v += 128) {
+        const u32x4 a0 = pa[v], a1 = pa[v + 64], b0 = pb[v], b1 = pb[v + 64];
+        po[v] = merge_vec<T>(a0, b0, wa, wb);
+        po[v + 64] = merge_vec<T>(a1, b1, wa, wb);
     }
+    if (v < vr) po[v] = merge_vec<T>(pa[v], pb[v], wa, wb);
     if (lane == 0) lse_out[row] = L;
 }
 
@@ -198,20 +183,23 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restri
 
 template <MergeOut T>
 hipError_t launch_merge_typed(const MergeArgs& a) {
-    const int D = (int)a.D;
-    const int tpr = D / 8;
-    if (tpr > 64) {
+    constexpr int osz = T == MergeOut::F32 ? 4 : 2;
+    const int vr = (int)(a.D * osz / 16);   // 16-byte vectors per row (the entry point checks divisibility)
+    if (vr > 64) {
         const int64_t blocks = (a.rows + 3) / 4;
         hipLaunchKernelGGL(attn_merge_wide_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
-                           a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D);
+                           a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, vr);
         return hipGetLastError();
     }
-    constexpr int MU = 1;   // row groups per wave (measured best on MI355X)
-    const int rpw = 64 / tpr;
+    // Row groups per wave.  Measured on MI355X, f32 O [1,24,5520,128] in place: 32.8 us with one,
+    // 33.2 with two, 38.8 with four (and 38.3 before the vector layout, whose f32 loads and stores
+    // each covered every other 16 bytes of a row).  16-bit O: 18.2 us with one, two or four.
+    constexpr int MU = 1;
+    const int rpw = 64 / vr;
     const int64_t waves = (a.rows + (int64_t)rpw * MU - 1) / ((int64_t)rpw * MU);
     const int64_t blocks = (waves + 3) / 4;
     hipLaunchKernelGGL((attn_merge_kernel<T, MU>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
-                       a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, D, rpw);
+                       a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, vr, rpw);
     return hipGetLastError();
 }
 

@@ -20,10 +20,13 @@ def _partials(seed, B=1, H=3, S=300, D=128, lse_spread=4.0):
     return oa, la, ob, lb
 
 
-@pytest.mark.parametrize("D", [64, 128, 8, 200])
+# 16-byte vectors per f32 row = D/4: 32, 16 and 2 (several rows per wave), 50 (one row, lanes
+# idle), 3 and 5 (D not a multiple of 8), 129 and 256 (the path for rows of more than 64 vectors,
+# with and without an odd last vector).  301 rows per head: a ragged last wave.
+@pytest.mark.parametrize("D", [64, 128, 8, 200, 12, 20, 516, 1024])
 def test_merge_f32(D):
     log(f"case: merge f32 D{D}")
-    oa, la, ob, lb = _partials(1 + D, D=D)
+    oa, la, ob, lb = _partials(1 + D, D=D, S=301)
     # a few rows with one or both sides empty
     la[0, 0, :3] = -np.inf
     oa[0, 0, :3] = 0
@@ -40,10 +43,20 @@ def test_merge_f32(D):
     assert np.max(np.abs(og - O)) <= 2e-6
     assert np.max(np.abs(lg[fin] - L[fin])) <= 2e-6
     assert np.all(og[0, 2, 9] == 0)
+    # in place into the first operand: the same bits as the separate output
+    ta, tla = dev_f32(oa), dev_f32(la)
+    cp.attn_merge(ta, tla, dev_f32(ob), dev_f32(lb), o_out=ta, lse_out=tla)
+    torch.cuda.synchronize()
+    assert torch.equal(ta.view(torch.int32), o.view(torch.int32))
+    assert torch.equal(tla.view(torch.int32), l.view(torch.int32))
 
 
-def test_merge_bf16_and_in_place():
-    oa, la, ob, lb = _partials(7)
+# 16-byte vectors per bf16 row = D/8: 16 (four rows per wave), 3, and 65 and 128 (the path for
+# rows of more than 64 vectors).
+@pytest.mark.parametrize("D", [128, 24, 520, 1024])
+def test_merge_bf16_and_in_place(D):
+    log(f"case: merge bf16 D{D}")
+    oa, la, ob, lb = _partials(7 + D, D=D)
     oab = inputs.f32_to_bf16_bits(oa)
     obb = inputs.f32_to_bf16_bits(ob)
     O, L = oracle.merge(f64_of_bf16(oab), la, f64_of_bf16(obb), lb)
