@@ -34,14 +34,14 @@ Pins: see tests/test_oracle.py (brute force, closed forms, invariants,
 library special cases, merge algebra, relayout bijections, RMSNorm closed
 forms and torch's rms_norm, 16-bit rounding ties).
 """
-from .attention import attention, attention_rows, lse_natural
+from .attention import attention, attention_rows
 from .merge import merge
 from .relayout import ulysses_pack, ulysses_unpack, alltoall, SEQ_TO_HEAD, HEAD_TO_SEQ
 from .qk_norm import rms_norm, qk_prologue, round_to_f16, round_to_bf16
 from .fp8 import e4m3_to_f64
 
 __all__ = [
-    "attention", "attention_rows", "lse_natural", "merge",
+    "attention", "attention_rows", "merge",
     "ulysses_pack", "ulysses_unpack", "alltoall", "SEQ_TO_HEAD", "HEAD_TO_SEQ",
     "rms_norm", "qk_prologue", "round_to_f16", "round_to_bf16", "e4m3_to_f64",
 ]

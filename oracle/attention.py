@@ -83,11 +83,3 @@ def attention_rows(q, k, v, scale: float, rows, row_block: int = 256):
     qs = np.asarray(q)[:, :, rows, :]
     return attention(qs, k, v, scale, row_block=row_block)
 
-
-def lse_natural(z: np.ndarray) -> np.ndarray:
-    """ln sum exp along the last axis (max-shifted); -inf for an empty axis."""
-    z = np.asarray(z, dtype=np.float64)
-    if z.shape[-1] == 0:
-        return np.full(z.shape[:-1], -np.inf)
-    m = z.max(axis=-1)
-    return m + np.log(np.exp(z - m[..., None]).sum(axis=-1))

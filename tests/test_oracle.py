@@ -8,6 +8,7 @@ relayout.  ``test_pins_catch_planted_mistakes`` plants plausible mistakes in
 copies of the oracle and checks that at least one pin fails for each.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -474,17 +475,52 @@ def test_16bit_rounding_ties_and_library():
     tb = torch.from_numpy(z).to(torch.bfloat16).to(torch.float64).numpy()
     np.testing.assert_array_equal(oracle.round_to_bf16(z64), tb)
     # on float64 inputs: the nearest representable value by exact rational distance, ties to even
-    from fractions import Fraction
     w = np.random.Generator(np.random.PCG64(907)).standard_normal(300) * 3.0
     for x in w:
-        for got, bits in ((float(oracle.round_to_f16(x)), 11), (float(oracle.round_to_bf16(x)), 8)):
-            m, e = math.frexp(x)
-            step = Fraction(2) ** (e - bits)                 # spacing of the type in x's binade
-            lo = (Fraction(x) / step).__floor__() * step
-            hi = lo + step
-            d_lo, d_hi = Fraction(x) - lo, hi - Fraction(x)
-            want = lo if d_lo < d_hi else hi if d_hi < d_lo else (lo if (lo / step) % 2 == 0 else hi)
-            assert Fraction(got) == want, (x, got, float(want))
+        assert Fraction(float(oracle.round_to_f16(x))) == exact_round(Fraction(float(x)), "f16"), x
+        assert Fraction(float(oracle.round_to_bf16(x))) == exact_round(Fraction(float(x)), "bf16"), x
+
+
+# significand bits (with the hidden bit) and the smallest spacing of each 16-bit type
+_FMT16 = {"f16": (11, Fraction(1, 2 ** 24)), "bf16": (8, Fraction(1, 2 ** 133))}
+
+
+def exact_round(x: Fraction, fmt: str) -> Fraction:
+    """x rounded to the nearest value of the 16-bit type `fmt`, ties to the even significand,
+    by exact rational arithmetic (finite, non-overflowing x).  Written from the definition of
+    the binary formats: in the binade [2^(e-1), 2^e) the spacing is 2^(e - bits), and below the
+    normal range it is the fixed subnormal spacing."""
+    bits, min_step = _FMT16[fmt]
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^(e-1) <= a < 2^(e+1)
+    while Fraction(2) ** e <= a:
+        e += 1
+    while Fraction(2) ** (e - 1) > a:
+        e -= 1
+    step = max(Fraction(2) ** (e - bits), min_step)
+    n = a / step
+    lo = n.numerator // n.denominator
+    frac = n - lo
+    k = lo + 1 if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and lo % 2 == 1) else lo
+    r = k * step
+    return r if x > 0 else -r
+
+
+def test_exact_round_by_hand():
+    """The test's own rounder on values whose rounding is known by hand."""
+    F = Fraction
+    assert exact_round(F(1) + F(1, 2 ** 11), "f16") == 1                    # tie -> even
+    assert exact_round(F(1) + F(3, 2 ** 11), "f16") == F(1) + F(1, 2 ** 9)  # tie -> even (up)
+    assert exact_round(F(1) + F(1, 2 ** 11) + F(1, 2 ** 40), "f16") == F(1) + F(1, 2 ** 10)
+    assert exact_round(F(-3, 2 ** 25), "f16") == F(-1, 2 ** 23)              # subnormal: 1.5 steps -> 2 (even)
+    assert exact_round(F(3, 2 ** 26), "f16") == F(1, 2 ** 24)                # subnormal: 0.75 step -> 1
+    assert exact_round(F(1, 2 ** 25), "f16") == 0                           # half the smallest step -> 0
+    assert exact_round(F(1) + F(1, 2 ** 8), "bf16") == 1
+    assert exact_round(F(1) + F(3, 2 ** 8), "bf16") == F(1) + F(1, 2 ** 6)
+    assert exact_round(F(255, 2 ** 7), "bf16") == F(255, 2 ** 7)            # 1.9921875: 8 bits hold it
+    assert exact_round(F(511, 2 ** 8), "bf16") == 2                         # 1.99609375: tie -> 2
 
 
 def test_qk_prologue_steps():
@@ -507,6 +543,61 @@ def test_qk_prologue_steps():
     assert np.all(np.abs(y0 - exact) <= 0.5 * ulp + 1e-300)
     # the scale split over Q and K recovers the 1/sqrt(D) score scale to fp16 accuracy
     assert abs(s16 * s16 - 128 ** -0.5) < 2e-4
+
+
+def pin_prologue_constant_rows(prologue):
+    """Closed form of both roundings.  A constant row c with eps = 0 has mean(x^2) = c^2, so the
+    exact RMSNorm output is sign(c) * w (c^2 and the mean over a power-of-two D are exact in
+    float64); w holds 16-bit values, so the first rounding returns sign(c) * w unchanged, and the
+    result must be the single rounding of sign(c) * w * s16, where s16 is post_scale rounded to
+    the 16-bit type.  Expected values come from exact rational rounding."""
+    g = np.random.Generator(np.random.PCG64(912))
+    for fmt, np16 in (("f16", np.float16), ("bf16", None)):
+        D = 128
+        w64 = g.standard_normal(D) * 2.0
+        if np16 is not None:
+            w64 = w64.astype(np16).astype(np.float64)
+        else:
+            w64 = np.array([float(exact_round(Fraction(float(x)), "bf16")) for x in w64])
+        for c in (1.5, -0.375, 3.0, -7.0):
+            x = np.full((1, D), c)
+            for ps in (D ** -0.25, 0.1, 3.3, 1.0 / 3.0):
+                s16 = exact_round(Fraction(float(ps)), fmt)
+                got = prologue(x, w64, 0.0, ps, fmt)
+                sgn = 1 if c > 0 else -1
+                want = [float(exact_round(sgn * Fraction(float(wd)) * s16, fmt)) for wd in w64]
+                np.testing.assert_array_equal(np.asarray(got, np.float64)[0], want)
+
+
+def test_qk_prologue_second_rounding_closed_form():
+    pin_prologue_constant_rows(lambda x, w, eps, ps, fmt: oracle.qk_prologue(x, w, eps, ps, dtype=fmt))
+
+
+def _prologue_mutant(kind):
+    """Plausible mistakes in the prologue's second step (planted in a copy, on the CPU)."""
+    def f(x, w, eps, ps, fmt):
+        r = oracle.round_to_f16 if fmt == "f16" else oracle.round_to_bf16
+        n16 = np.asarray(r(oracle.rms_norm(x, w, eps)), np.float64)
+        s16 = float(np.asarray(r(np.float64(ps)), np.float64))
+        if kind == "no_second_rounding":
+            return n16 * s16
+        if kind == "unrounded_constant":
+            return np.asarray(r(n16 * ps), np.float64)
+        if kind == "truncate":
+            y = n16 * s16
+            t = np.asarray(r(y), np.float64)
+            return np.where(np.abs(t) > np.abs(y), np.nextafter(t, 0) if fmt == "bf16" else
+                            np.asarray(np.nextafter(t.astype(np.float16), np.float16(0)), np.float64), t)
+        if kind == "scale_before_norm":
+            return np.asarray(r(oracle.rms_norm(np.asarray(x) * s16, w, eps)), np.float64)
+        raise ValueError(kind)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["no_second_rounding", "unrounded_constant", "truncate", "scale_before_norm"])
+def test_prologue_pin_catches_planted_mistakes(kind):
+    with pytest.raises(AssertionError):
+        pin_prologue_constant_rows(_prologue_mutant(kind))
 
 
 def test_p4_inputs_recipe():
