@@ -240,11 +240,20 @@ def qk_rmsnorm(x, w, eps=1e-6, post_scale=1.0, out=None, stream=None):
 
 
 def _relayout_shapes(src, P, direction, pack):
+    """((B, S_local, H, D), dst shape) of a relayout; refuses shapes the index maps do not cover
+    (the C ABI sees only S_local and H, so a full sequence that P does not divide must be caught
+    here)."""
+    if P < 1:
+        raise ValueError(f"P must be >= 1, got {P}")
     if pack and direction == SEQ_TO_HEAD:
         B, S_l, H, D = src.shape
+        if H % P:
+            raise ValueError(f"heads ({H}) must be divisible by P ({P})")
         return (B, S_l, H, D), (B, P, S_l, H // P, D)
     if pack and direction == HEAD_TO_SEQ:
         B, Hp, S, D = src.shape
+        if S % P:
+            raise ValueError(f"sequence length ({S}) must be divisible by P ({P})")
         return (B, S // P, Hp * P, D), (B, P, S // P, Hp, D)
     B, P2, S_l, Hp, D = src.shape
     if P2 != P:

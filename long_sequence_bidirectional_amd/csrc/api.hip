@@ -388,6 +388,8 @@ CPATTN_EXPORT cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_
     const int64_t rows = prod({B, H, S});
     const int64_t elems = prod({B, H, S, D});
     if (rows < 0 || elems < 0 || rows > (kMaxDim - 1) * 4) return CPATTN_E_SHAPE;
+    // one launch holds fewer than 2^32 work-items
+    if (cpattn::attn_merge_blocks(rows, D, merge_out(odt)) * 256 > (int64_t)UINT32_MAX) return CPATTN_E_SHAPE;
     if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out) || !aligned16(lse_a) || !aligned16(lse_b) ||
         !aligned16(lse_out))
         return CPATTN_E_ALIGN;
@@ -454,9 +456,8 @@ cpattn_status relayout(const void* src, void* dst, int64_t B, int64_t S_local, i
     if (row_bytes % 16 != 0) return CPATTN_E_HEADDIM;
     const int64_t n_rows = prod({B, S_local, H});
     const int64_t bytes = mul_checked(n_rows, row_bytes);
-    // 32-bit row indices in the kernel; one thread per 16-byte chunk.
-    if (n_rows < 0 || bytes < 0 || n_rows > (int64_t)UINT32_MAX || bytes / 16 / 256 >= kMaxDim)
-        return CPATTN_E_SHAPE;
+    // 32-bit row indices in the kernel (its grid strides over the chunks, so their count is free)
+    if (n_rows < 0 || bytes < 0 || n_rows > (int64_t)UINT32_MAX) return CPATTN_E_SHAPE;
     if (!aligned16(src) || !aligned16(dst)) return CPATTN_E_ALIGN;
     if (overlap(range(src, bytes), range(dst, bytes))) return CPATTN_E_ALIAS;
     const int mode = (dir == CPATTN_SEQ_TO_HEAD ? 0 : 2) + (pack ? 0 : 1);

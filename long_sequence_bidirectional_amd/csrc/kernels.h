@@ -123,6 +123,11 @@ struct MergeArgs {
 
 hipError_t launch_attn_merge(const MergeArgs& a);
 
+// Workgroups (256 work-items each) launch_attn_merge uses for `rows` rows of D values of type t.
+// A launch holds fewer than 2^32 work-items, so the entry point refuses shapes with
+// attn_merge_blocks(...) * 256 >= 2^32.
+int64_t attn_merge_blocks(int64_t rows, int64_t D, MergeOut t);
+
 // RMSNorm over rows of D 16-bit values, times w, rounded to the 16-bit type, then
 // (has_scale) times the 16-bit constant scale16 and rounded again.
 struct QkNormArgs {

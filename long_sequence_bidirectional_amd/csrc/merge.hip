@@ -181,24 +181,31 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restri
 
 }  // namespace
 
+// Row groups per wave of the fast path.  Measured on MI355X, f32 O [1,24,5520,128] in place:
+// 32.8 us with one, 33.2 with two, 38.8 with four (and 38.3 before the vector layout, whose f32
+// loads and stores each covered every other 16 bytes of a row).  16-bit O: 18.2 us with one, two
+// or four.
+constexpr int kMergeMU = 1;
+
+int64_t attn_merge_blocks(int64_t rows, int64_t D, MergeOut t) {
+    const int64_t vr = D * (t == MergeOut::F32 ? 4 : 2) / 16;   // 16-byte vectors per row
+    if (vr > 64) return (rows + 3) / 4;                         // one row per wave
+    const int64_t per_wave = (64 / vr) * kMergeMU;
+    return ((rows + per_wave - 1) / per_wave + 3) / 4;
+}
+
 template <MergeOut T>
 hipError_t launch_merge_typed(const MergeArgs& a) {
     constexpr int osz = T == MergeOut::F32 ? 4 : 2;
     const int vr = (int)(a.D * osz / 16);   // 16-byte vectors per row (the entry point checks divisibility)
+    const int64_t blocks = attn_merge_blocks(a.rows, a.D, T);   // the entry point keeps blocks * 256 < 2^32
     if (vr > 64) {
-        const int64_t blocks = (a.rows + 3) / 4;
         hipLaunchKernelGGL(attn_merge_wide_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
                            a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, vr);
         return hipGetLastError();
     }
-    // Row groups per wave.  Measured on MI355X, f32 O [1,24,5520,128] in place: 32.8 us with one,
-    // 33.2 with two, 38.8 with four (and 38.3 before the vector layout, whose f32 loads and stores
-    // each covered every other 16 bytes of a row).  16-bit O: 18.2 us with one, two or four.
-    constexpr int MU = 1;
     const int rpw = 64 / vr;
-    const int64_t waves = (a.rows + (int64_t)rpw * MU - 1) / ((int64_t)rpw * MU);
-    const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((attn_merge_kernel<T, MU>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
+    hipLaunchKernelGGL((attn_merge_kernel<T, kMergeMU>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.o_a,
                        a.lse_a, a.o_b, a.lse_b, a.o_out, a.lse_out, a.rows, vr, rpw);
     return hipGetLastError();
 }

@@ -85,10 +85,17 @@ __global__ __launch_bounds__(256) void relayout_kernel(const u32x4* __restrict__
 
 __global__ __launch_bounds__(256) void fill_empty_kernel(u32x4* __restrict__ o, uint64_t o_chunks,
                                                          float* __restrict__ lse, uint64_t n_rows) {
-    const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid < o_chunks) o[gid] = u32x4{0, 0, 0, 0};
-    if (gid < n_rows) lse[gid] = -INFINITY;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < o_chunks || gid < n_rows;
+         gid += stride) {
+        if (gid < o_chunks) o[gid] = u32x4{0, 0, 0, 0};
+        if (gid < n_rows) lse[gid] = -INFINITY;
+    }
 }
+
+// Both kernels above walk their range with a grid stride, so a launch is capped at this many
+// workgroups (2^30 work-items, inside the 2^32 a launch may hold) and any size still fits.
+constexpr uint64_t kMaxStrideBlocks = uint64_t(1) << 22;
 
 }  // namespace
 
@@ -97,7 +104,8 @@ hipError_t launch_relayout(const RelayoutArgs& a) {
     const uint32_t chunks = (uint32_t)(a.row_bytes / 16);
     const uint32_t n_rows = (uint32_t)(a.B * a.S_local * a.H);
     const uint64_t total = (uint64_t)n_rows * chunks;
-    const uint64_t blocks = (total + 256 * UNROLL - 1) / (256 * UNROLL);
+    uint64_t blocks = (total + 256 * UNROLL - 1) / (256 * UNROLL);
+    if (blocks > kMaxStrideBlocks) blocks = kMaxStrideBlocks;
     hipLaunchKernelGGL(relayout_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream,
                        static_cast<const u32x4*>(a.src), static_cast<u32x4*>(a.dst), n_rows, chunks, a.mode,
                        (uint32_t)a.S_local, (uint32_t)a.H, Hp, (uint32_t)a.P);
@@ -107,7 +115,8 @@ hipError_t launch_relayout(const RelayoutArgs& a) {
 hipError_t launch_fill_empty(void* o, int64_t o_bytes, float* lse, int64_t n_rows, hipStream_t stream) {
     const uint64_t chunks = (uint64_t)o_bytes / 16;
     const uint64_t n = chunks > (uint64_t)n_rows ? chunks : (uint64_t)n_rows;
-    const uint64_t blocks = (n + 255) / 256;
+    uint64_t blocks = (n + 255) / 256;
+    if (blocks > kMaxStrideBlocks) blocks = kMaxStrideBlocks;
     hipLaunchKernelGGL(fill_empty_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<u32x4*>(o),
                        chunks, lse, (uint64_t)n_rows);
     return hipGetLastError();

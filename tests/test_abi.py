@@ -214,6 +214,39 @@ def test_attn_merge_validation(L):
     assert merge(L, oo=B_) == _lib.E_ALIAS             # o_out on top of lse_a
 
 
+def test_attn_merge_launch_size_limit(L):
+    """A merge launch holds fewer than 2^32 work-items; larger shapes are refused as E_SHAPE
+    before any HIP call (only the refusing side is probed: these fake buffers must never reach a
+    kernel).  Work-items per launch: 256 per workgroup; f32 D=128 rows take 2 rows per wave and
+    4 waves per workgroup, bf16 D=8 rows 64 per wave, f32 D=1024 rows one wave each."""
+    far = [(i + 1) << 40 for i in range(6)]              # 1 TiB apart: no overlap at these sizes
+    lim_wg = (1 << 24) - 1                                 # workgroups of 256 below 2^32 work-items
+    for D, dt, rows_per_wg in ((128, _lib.F32, 8), (8, _lib.BF16, 256), (1024, _lib.F32, 4)):
+        rows = lim_wg * rows_per_wg + 2                    # one workgroup more than fits
+        st = L.cpattn_attn_merge(*far, 1, 2, rows // 2, D, dt, None)
+        assert st == _lib.E_SHAPE, (D, dt, st)
+
+
+def test_relayout_row_index_limit(L):
+    # more than 2^32 rows of D values do not fit the kernel's 32-bit row indices
+    assert rl(L, "cpattn_ulysses_pack", src=1 << 40, dst=1 << 44, S_l=(1 << 31) - 1, H=8, P=8) == _lib.E_SHAPE
+
+
+def test_binding_refuses_undivided_relayout():
+    """The binding derives S_local = S // P for a head->seq pack: an S that P does not divide
+    would be read with the wrong per-head stride, so it is refused before any device call (as
+    the oracle refuses it); likewise a head count that P does not divide."""
+    import torch
+    import long_sequence_bidirectional_amd as cp
+    with pytest.raises(ValueError, match="divisible"):
+        cp.ulysses_pack(torch.zeros((1, 3, 100, 128), dtype=torch.bfloat16), 8, cp.HEAD_TO_SEQ)
+    with pytest.raises(ValueError, match="divisible"):
+        cp.ulysses_pack(torch.zeros((1, 10, 20, 128), dtype=torch.bfloat16), 8, cp.SEQ_TO_HEAD)
+    import oracle
+    with pytest.raises(ValueError):
+        oracle.ulysses_pack(torch.zeros((1, 3, 100, 128)).numpy(), 8, oracle.HEAD_TO_SEQ)
+
+
 def ring(L, q=A, k=B_, v=C, o=D_, lse=E, ow=0x60000000, lw=0x70000000, n=8, Skv=64, D=128, scale=0.1):
     return L.cpattn_ring_attn_fwd(q, k, v, o, lse, ow, lw, 1, 2, 64, Skv, n, D, scale, None)
 
