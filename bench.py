@@ -77,9 +77,11 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true", help="skip merge/ring/relayout measurements")
     ap.add_argument("--traffic", type=str, default=TRAFFIC_FILE,
                     help="JSON with the measured HBM bytes per launch of the dominant kernel")
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="run one self-attention launch and one calibration copy, print nothing else "
-                         "(the program profiled by the rocprofv3 --pmc passes)")
+    ap.add_argument("--profile-pass", nargs="?", const="all", choices=["all", "short"], default=None,
+                    help="the program profiled by the rocprofv3 --pmc passes, instead of the bench: 'all' runs "
+                         "one self-attention launch, one calibration copy and the other kernels once; 'short' "
+                         "runs one launch of each short-key-range shape (cross-attention, AllGather-KV rank, "
+                         "ring chunks) and the calibration copy")
     return ap.parse_args()
 
 
@@ -175,6 +177,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
     q, k, v, kt, vt = (dev(g[n]) for n in ("q", "k", "v", "k_text", "v_text"))
+    if args.profile_pass == "short":
+        profile_pass_short(cp, torch, q, k, v, kt, vt)
+        return
     if args.profile_pass:
         profile_pass(cp, torch, q, k, v)
         return
@@ -233,7 +238,7 @@ def main():
 
     traffic, counters = measured_counters(args.traffic)
 
-    secondary = None if args.no_secondary else secondary_rows(cp, torch, q, k, v, stream)
+    secondary = None if args.no_secondary else secondary_rows(cp, torch, q, k, v, stream, kt, vt)
 
     result = {
         "metric": "attention TFLOP/s (bf16) and % of MFMA peak at S=44160, H=24, D=128",
@@ -275,8 +280,8 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def workspace(cp, torch, B, H, Sq, Skv, D):
-    n = cp.attn_fwd_workspace_size(B, H, Sq, Skv, D)
+def workspace(cp, torch, B, H, Sq, Skv, D, f32_out=False):
+    n = cp.attn_fwd_workspace_size(B, H, Sq, Skv, D, o_dtype=cp.F32 if f32_out else cp.BF16)
     return torch.empty(n, dtype=torch.uint8, device="cuda")
 
 
@@ -347,7 +352,96 @@ def profile_pass(cp, torch, q, k, v):
           f"{x.numel() * 2} bytes", flush=True)
 
 
-def secondary_rows(cp, torch, q, k, v, stream):
+def timed_leg(torch, stream, fn, flops=None, nbytes=None, iters=50, warmup=3, clock=True):
+    """`warmup` untimed calls, then `iters` calls each bracketed by its own HIP event pair on the
+    launch stream: mean / median / min / max per call, the throughput of the median call, and one
+    amd-smi power and clock reading taken while the same call keeps running (the kernels run at
+    the board's power limit, so the clock belongs to the result)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    pairs = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(elapsed_ms(pairs))
+    med = ms[len(ms) // 2]
+    out = {"iters": iters, "warmup": warmup, "ms_mean": round(sum(ms) / len(ms), 4), "ms_median": round(med, 4),
+           "ms_min": round(ms[0], 4), "ms_max": round(ms[-1], 4)}
+    if flops is not None:
+        out["tflops_median"] = round(flops / med / 1e9, 1)
+        out["frac_of_bf16_peak"] = round(flops / med / 1e9 / PEAK_BF16_TFLOPS, 4)
+    if nbytes is not None:
+        out["GBps_median"] = round(nbytes / med / 1e6, 1)
+    if clock:
+        sample = []
+        th = threading.Thread(target=lambda: sample.append(smi_sample()), daemon=True)
+        th.start()
+        while th.is_alive():      # keep this leg's kernel running until the reading is back
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+        th.join()
+        pc = sample[0] if sample else None
+        out["socket_power_w"] = pc[0] if pc else None
+        out["gfx_clock_mhz"] = round(pc[1]) if pc else None
+    return out
+
+
+def calibration_copy(cp, torch):
+    """The copy of known size the HBM counters are scaled by: a Ulysses pack of a [44160,24,128]
+    bf16 shard, 271,319,040 bytes read and the same written."""
+    shard = torch.empty(CALIB_SHAPE, dtype=torch.bfloat16, device="cuda").view(torch.int16).random_().view(
+        torch.bfloat16)
+    send = torch.empty((1, 8, CALIB_SHAPE[1], CALIB_SHAPE[2] // 8, CALIB_SHAPE[3]), dtype=torch.bfloat16,
+                       device="cuda")
+    torch.cuda.synchronize()
+    cp.ulysses_pack(shard, 8, cp.SEQ_TO_HEAD, dst=send)
+    torch.cuda.synchronize()
+
+
+def profile_pass_short(cp, torch, q, k, v, kt, vt):
+    """One launch of each short-key-range shape, in this order (each attention launch followed
+    by its piece merge): cross-attention 44160 x 2992 (bf16 O), the AllGather-KV rank 5520 x 44160
+    (bf16 O), ring chunk 0 then ring chunk 1 folded in by the accumulate epilogue (5520 x 5520,
+    f32 O); then the calibration copy."""
+    from long_sequence_bidirectional_amd import inputs
+    S_L, H, D = inputs.S_LOCAL, inputs.N_HEADS, inputs.HEAD_DIM
+    legend = []
+    o = torch.empty_like(q)
+    l = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    cp.attn_fwd_ex(q, kt, vt, o=o, lse=l, workspace=workspace(cp, torch, 1, H, q.shape[2], kt.shape[2], D))
+    torch.cuda.synchronize()
+    legend.append("cross 44160x2992")
+    del o, l
+    q_l = q[:, :, :S_L].contiguous()
+    o_b = torch.empty((1, H, S_L, D), dtype=torch.bfloat16, device="cuda")
+    l = torch.empty((1, H, S_L), dtype=torch.float32, device="cuda")
+    ws = workspace(cp, torch, 1, H, S_L, inputs.S_VIDEO, D)
+    torch.cuda.synchronize()
+    cp.attn_fwd_ex(q_l, k, v, o=o_b, lse=l, workspace=ws)
+    torch.cuda.synchronize()
+    legend.append("allgather_kv_rank 5520x44160")
+    kc = [k[:, :, c * S_L:(c + 1) * S_L].contiguous() for c in range(2)]
+    vc = [v[:, :, c * S_L:(c + 1) * S_L].contiguous() for c in range(2)]
+    o_f = torch.empty((1, H, S_L, D), dtype=torch.float32, device="cuda")
+    ws_c = workspace(cp, torch, 1, H, S_L, S_L, D, f32_out=True)
+    torch.cuda.synchronize()
+    for c in range(2):
+        cp.attn_fwd_ex(q_l, kc[c], vc[c], o=o_f, lse=l, workspace=ws_c, accumulate=c > 0)
+        torch.cuda.synchronize()
+        legend.append(f"ring chunk {c} 5520x5520{' (accumulate)' if c else ''}")
+    calibration_copy(cp, torch)
+    print("profile pass (short key ranges) done: " + "; ".join(legend) + "; calibration copy "
+          f"{CALIB_SHAPE[1] * CALIB_SHAPE[2] * CALIB_SHAPE[3] * 2} bytes read and written", flush=True)
+
+
+def secondary_rows(cp, torch, q, k, v, stream, kt=None, vt=None):
     """Timings of the other kernels on the path, at their per-rank shapes."""
     from long_sequence_bidirectional_amd import inputs
     S_L, P, H, D = inputs.S_LOCAL, inputs.CP_DEGREE, inputs.N_HEADS, inputs.HEAD_DIM
@@ -364,6 +458,7 @@ def secondary_rows(cp, torch, q, k, v, stream):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / iters
 
+    # The per-rank legs: 3 warm-ups, then 50 calls each timed on its own, median reported.
     # ring_rank: Q 5520 rows vs 8 chunks of 5520 keys (chunk attention folded into the f32
     # accumulator in its epilogue; the work buffers hold the split pieces)
     q_l = q[:, :, :S_L].contiguous()
@@ -373,28 +468,34 @@ def secondary_rows(cp, torch, q, k, v, stream):
     l = torch.empty((1, H, S_L), dtype=torch.float32, device="cuda")
     ow, lw = torch.empty_like(o), torch.empty_like(l)
     ring_flops = 4.0 * H * S_L * S_L * P * D
-    ms = timeit(lambda: cp.ring_attn_fwd(q_l, kc, vc, o=o, lse=l, o_work=ow, lse_work=lw, stream=stream), 5)
-    out["ring_rank_tflops"] = round(ring_flops / ms / 1e9, 1)
-    ms = timeit(lambda: cp.ring_attn_fwd(q_l, kc, vc, o=o, lse=l, use_work=False, stream=stream), 5)
-    out["ring_rank_unsplit_tflops"] = round(ring_flops / ms / 1e9, 1)
+    out["ring_rank"] = timed_leg(torch, stream, lambda: cp.ring_attn_fwd(q_l, kc, vc, o=o, lse=l, o_work=ow,
+                                                                          lse_work=lw, stream=stream), ring_flops)
+    out["ring_rank_unsplit"] = timed_leg(
+        torch, stream, lambda: cp.ring_attn_fwd(q_l, kc, vc, o=o, lse=l, use_work=False, stream=stream), ring_flops,
+        clock=False)
+    # one chunk's attention alone (the ring step's kernel), accumulating into the f32 result
+    ws_c = workspace(cp, torch, 1, H, S_L, S_L, D, f32_out=True)
+    out["ring_chunk"] = timed_leg(torch, stream, lambda: cp.attn_fwd_ex(q_l, kc[3], vc[3], o=o, lse=l, workspace=ws_c,
+                                                                        accumulate=True, stream=stream),
+                                  ring_flops / P, clock=False)
     # allgather_kv_rank: Q 5520 vs K/V 44160
     o_b = torch.empty((1, H, S_L, D), dtype=torch.bfloat16, device="cuda")
     ws = workspace(cp, torch, 1, H, S_L, inputs.S_VIDEO, D)
     agkv_flops = 4.0 * H * S_L * inputs.S_VIDEO * D
-    ms = timeit(lambda: cp.attn_fwd_ex(q_l, k, v, o=o_b, lse=l, workspace=ws, stream=stream), 5)
-    out["allgather_kv_rank_tflops"] = round(agkv_flops / ms / 1e9, 1)
-    ms = timeit(lambda: cp.attn_fwd(q_l, k, v, o=o_b, lse=l, stream=stream), 5)
-    out["allgather_kv_rank_unsplit_tflops"] = round(agkv_flops / ms / 1e9, 1)
+    out["allgather_kv_rank"] = timed_leg(
+        torch, stream, lambda: cp.attn_fwd_ex(q_l, k, v, o=o_b, lse=l, workspace=ws, stream=stream), agkv_flops)
+    out["allgather_kv_rank_unsplit"] = timed_leg(
+        torch, stream, lambda: cp.attn_fwd(q_l, k, v, o=o_b, lse=l, stream=stream), agkv_flops, clock=False)
     # ulysses_rank attention: H=3, S=44160
     q3, k3, v3 = (x[:, :3].contiguous() for x in (q, k, v))
     o3 = torch.empty_like(q3)
     l3 = torch.empty((1, 3, inputs.S_VIDEO), dtype=torch.float32, device="cuda")
     ws3 = workspace(cp, torch, 1, 3, inputs.S_VIDEO, inputs.S_VIDEO, D)
     uly_flops = 4.0 * 3 * inputs.S_VIDEO ** 2 * D
-    ms = timeit(lambda: cp.attn_fwd_ex(q3, k3, v3, o=o3, lse=l3, workspace=ws3, stream=stream), 5)
-    out["ulysses_rank_tflops"] = round(uly_flops / ms / 1e9, 1)
-    ms = timeit(lambda: cp.attn_fwd(q3, k3, v3, o=o3, lse=l3, stream=stream), 5)
-    out["ulysses_rank_unsplit_tflops"] = round(uly_flops / ms / 1e9, 1)
+    out["ulysses_rank"] = timed_leg(
+        torch, stream, lambda: cp.attn_fwd_ex(q3, k3, v3, o=o3, lse=l3, workspace=ws3, stream=stream), uly_flops)
+    out["ulysses_rank_unsplit"] = timed_leg(
+        torch, stream, lambda: cp.attn_fwd(q3, k3, v3, o=o3, lse=l3, stream=stream), uly_flops, clock=False)
     # the rank's local work between the two all-to-alls, from the receive buffers of Q, K, V
     # ([P, S_l, Hp, D] each) to the send buffer of O: unpack x3 + head-major attention + pack,
     # against sequence-major attention reading and writing those buffers in place
@@ -410,12 +511,19 @@ def secondary_rows(cp, torch, q, k, v, stream):
         cp.attn_fwd_ex(unpacked[0], unpacked[1], unpacked[2], o=o3, lse=l3, workspace=ws3, stream=stream)
         cp.ulysses_pack(o3, P, cp.HEAD_TO_SEQ, dst=o_send.view(1, P, S_L, H // P, D), stream=stream)
 
-    ms_unfused = timeit(unfused, 5)
-    ms_fused = timeit(lambda: cp.attn_fwd_ex(recv[0], recv[1], recv[2], o=o_send, lse=l3, workspace=ws3s,
-                                             seq_major=True, stream=stream), 5)
-    out["ulysses_rank_local_unfused_ms"] = round(ms_unfused, 3)
-    out["ulysses_rank_local_fused_ms"] = round(ms_fused, 3)
-    out["ulysses_rank_fused_tflops"] = round(uly_flops / ms_fused / 1e9, 1)
+    out["ulysses_rank_local_unfused"] = timed_leg(torch, stream, unfused, uly_flops, clock=False)
+    out["ulysses_rank_local_fused"] = timed_leg(
+        torch, stream, lambda: cp.attn_fwd_ex(recv[0], recv[1], recv[2], o=o_send, lse=l3, workspace=ws3s,
+                                              seq_major=True, stream=stream), uly_flops, clock=False)
+    # cross-attention of the video layer on its own: 44160 queries against the 2992 text keys
+    if kt is not None:
+        o_x = torch.empty_like(q)
+        l_x = torch.empty((1, H, inputs.S_VIDEO), dtype=torch.float32, device="cuda")
+        ws_x = workspace(cp, torch, 1, H, inputs.S_VIDEO, kt.shape[2], D)
+        out["cross_attention"] = timed_leg(
+            torch, stream, lambda: cp.attn_fwd_ex(q, kt, vt, o=o_x, lse=l_x, workspace=ws_x, stream=stream),
+            4.0 * H * inputs.S_VIDEO * kt.shape[2] * D)
+        del o_x, l_x, ws_x
     # merge (f32 O, the ring partial format): reads 2 O + 2 LSE, writes 1 O + 1 LSE
     ms = timeit(lambda: cp.attn_merge(o, l, ow, lw, o_out=o, lse_out=l, stream=stream))
     merge_bytes = 3 * o.numel() * 4 + 3 * l.numel() * 4
@@ -441,27 +549,20 @@ def secondary_rows(cp, torch, q, k, v, stream):
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 matrix-core peak (twice bf16)
 
 
-def fp8_rows(cp, torch, stream, iters=10):
+def fp8_rows(cp, torch, stream):
     """Self-attention S=44160, H=24, D=128 with E4M3 inputs (N(0,1) draws rounded to E4M3,
-    scales 1) on the fp8 matrix cores; O in bf16."""
-    import numpy as np
+    scales 1) on the fp8 matrix cores; O in bf16.  3 warm-ups, 50 calls timed one by one."""
     from long_sequence_bidirectional_amd import inputs
     S, H, D = inputs.S_VIDEO, inputs.N_HEADS, inputs.HEAD_DIM
     q8, k8, v8 = (torch.from_numpy(inputs.random_e4m3((1, H, S, D), 7300 + i)).cuda() for i in range(3))
     o = torch.empty((1, H, S, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, H, S), dtype=torch.float32, device="cuda")
-    fn = lambda: cp.attn_fwd_fp8(q8, k8, v8, o=o, lse=lse, stream=stream)
-    fn()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(iters):
-        fn()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / iters
-    tf = 4.0 * H * S * S * D / ms / 1e9
-    return {"fp8_self_ms": round(ms, 3), "fp8_self_tflops": round(tf, 1),
+    flops = 4.0 * H * S * S * D
+    leg = timed_leg(torch, stream, lambda: cp.attn_fwd_fp8(q8, k8, v8, o=o, lse=lse, stream=stream), flops)
+    tf = flops / leg["ms_median"] / 1e9
+    leg.pop("frac_of_bf16_peak", None)
+    leg["frac_of_fp8_peak"] = round(tf / PEAK_FP8_TFLOPS, 4)
+    return {"fp8_self": leg, "fp8_self_ms": leg["ms_median"], "fp8_self_tflops": round(tf, 1),
             "fp8_self_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
 
 

@@ -9,7 +9,7 @@ import oracle
 import long_sequence_bidirectional_amd as cp
 from long_sequence_bidirectional_amd import inputs
 from helpers import (assert_bf16_parity, assert_f32_parity, dev_bf16, dev_f32, f64_of_bf16, host64, log,
-                     scale_of, BF16_MAX_ABS)
+                     scale_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,20 +90,37 @@ def test_bf16_closed_forms():
     assert err <= 8e-3
 
 
-def test_bf16_large_scores_stay_finite():
-    # |scores| up to ~50 and beyond: checks the running-max shift
+@pytest.mark.parametrize("out_f32", [False, True], ids=["o_16", "o_f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_large_scores(dtype, out_f32):
+    """Q x 8: scores ~ N(0, 64), |score| up to ~40, so one or a few keys dominate each row and
+    later blocks often raise the running max.  Held to the stated gates.  Bound: the key that
+    set the running max has weight exactly 1, every other weight carries at most u relative
+    rounding (u = 2^-9 bf16, 2^-12 fp16) and a 16-bit O one more u, so |dO| <= 2 u max|v|
+    (~1.7e-2 bf16 at max|v| ~ 4.3; half that with an f32 O); the LSE depends on f32 scores
+    only (relative error ~1e-7 of |score| <= 40)."""
     D = 128
-    qb = inputs.random_bf16((1, 2, 256, D), 41, scale=8.0)
-    kb = inputs.random_bf16((1, 2, 500, D), 42)
-    vb = inputs.random_bf16((1, 2, 500, D), 43)
-    o, lse = cp.attn_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb))
+    log(f"case: large scores dtype={dtype} out_f32={out_f32}")
+    if dtype == "bf16":
+        qs = inputs.random_bf16((1, 2, 256, D), 41, scale=8.0)
+        ks = inputs.random_bf16((1, 2, 500, D), 42)
+        vs = inputs.random_bf16((1, 2, 500, D), 43)
+        dev, f64 = dev_bf16, f64_of_bf16
+    else:
+        qs = inputs.random_f16((1, 2, 256, D), 41, scale=8.0)
+        ks = inputs.random_f16((1, 2, 500, D), 42)
+        vs = inputs.random_f16((1, 2, 500, D), 43)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        f64 = lambda a: a.astype(np.float64)
+    o, lse = cp.attn_fwd(dev(qs), dev(ks), dev(vs), out_dtype=torch.float32 if out_f32 else None)
     torch.cuda.synchronize()
-    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+    O, L = oracle.attention(f64(qs), f64(ks), f64(vs), scale_of(D))
     og, lg = host64(o), host64(lse)
     assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg))
-    # sharp softmax: a single key dominates most rows, so O is close to one row of V
-    assert np.max(np.abs(og - O)) <= 3 * BF16_MAX_ABS
-    assert np.max(np.abs(lg - L)) <= 2e-2
+    assert_bf16_parity(og, lg, O, L, f"large scores {dtype}")
+    if dtype == "f16":   # 11 significant bits: the fp16 diagnostics
+        rel = float(np.linalg.norm(og - O) / np.linalg.norm(O))
+        assert rel <= 2e-3 and float(np.max(np.abs(lg - L))) <= 1e-4
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
