@@ -1,6 +1,6 @@
 /*
  * cpattn -- per-rank attention for context-parallel diffusion transformers
- * on AMD Instinct MI355X (gfx950).  C ABI, version 2.
+ * on AMD Instinct MI355X (gfx950).  C ABI, version 3.
  *
  * What the library computes (sources are the pages' titles and sections):
  *
@@ -48,10 +48,12 @@
  *
  *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous
  *    (row-major, last dimension fastest) and 16-byte aligned.  The library
- *    never allocates, frees or retains memory and has no handles; scratch
- *    memory, where a call can use it, is a caller-owned workspace argument.
- *    The only state kept between calls is a per-device cache of the number
- *    of attention workgroups the device holds at once.
+ *    never allocates, frees or retains caller memory and has no handles;
+ *    scratch memory, where a call can use it, is a caller-owned workspace
+ *    argument, except for cpattn_attn_fwd_ex_static, which uses a fixed
+ *    device array of the library's own.  The other state kept between calls
+ *    is a per-device cache of the number of attention workgroups the device
+ *    holds at once and of that array's device address.
  *  - Work is enqueued on the caller's HIP stream (0 = the null stream) and
  *    runs asynchronously; the call returns once the launches are enqueued.
  *  - Argument checks run synchronously, on the host, before any HIP call.
@@ -61,7 +63,8 @@
  *  - Sizes are int64_t; every element count must stay below 2^62 and every
  *    per-dimension size below 2^31.
  *  - Functions are reentrant and thread-safe.  Calls on different streams
- *    may run concurrently as long as their buffers do not overlap.
+ *    may run concurrently as long as their buffers do not overlap (for
+ *    cpattn_attn_fwd_ex_static that includes the library's scratch: see there).
  *
  * bf16 is the 16-bit brain-float format stored as raw 16-bit words; f16 is
  * IEEE binary16; f32 is IEEE binary32.
@@ -76,7 +79,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 2
+#define CPATTN_ABI_VERSION 3
 
 typedef enum {
     CPATTN_OK = 0,
@@ -175,6 +178,36 @@ cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, vo
                                  float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
                                  uint32_t flags, void* workspace, uint64_t workspace_bytes,
                                  hipStream_t stream);
+
+/*
+ * cpattn_attn_fwd_ex for callers that cannot allocate device memory -- code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation: the split workspace is the library's static scratch instead
+ * of a caller buffer, and the call allocates nothing.
+ *
+ * The scratch is a file-scope device array of CPATTN_STATIC_SCRATCH_BYTES
+ * (32 MiB), one per device, held from the first call on that device until
+ * the process ends; the first call on a device looks up its address there
+ * (CPATTN_E_HIP if HIP cannot give it).  scratch_bytes is how much of it the
+ * split may use, exactly as workspace_bytes for cpattn_attn_fwd_ex (0 = no
+ * split; cpattn_attn_fwd_workspace_size gives the best plan's size, and a
+ * smaller size only means fewer pieces); scratch_bytes above
+ * CPATTN_STATIC_SCRATCH_BYTES -> CPATTN_E_SHAPE.  Every other argument,
+ * check and result is that of cpattn_attn_fwd_ex: with the same
+ * scratch_bytes as workspace_bytes the outputs are the same bits.
+ *
+ * Nothing in the scratch needs clearing between calls: a call writes every
+ * byte its piece merge reads before reading it, in stream order.  All calls
+ * on one device share that device's scratch, so calls on one device must not
+ * overlap in time (issue them on one stream, or order the streams): two
+ * overlapping calls race on it.
+ */
+#define CPATTN_STATIC_SCRATCH_BYTES (32u << 20)
+
+cpattn_status cpattn_attn_fwd_ex_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
+                                        float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
+                                        uint32_t flags, uint64_t scratch_bytes, hipStream_t stream);
 
 /*
  * Attention with 8-bit float inputs (OCP FP8 E4M3), one f32 scale per tensor.

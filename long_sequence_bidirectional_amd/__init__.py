@@ -7,6 +7,7 @@ torch provides device memory and streams.
 
   attn_fwd(q, k, v, o=None, lse=None, scale=None)        -> (o, lse)
   attn_fwd_ex(q, k, v, o, lse, workspace=..., accumulate=False) -> (o, lse)
+  attn_fwd_ex_static(q, k, v, o, lse, scratch_bytes=None, ...) -> (o, lse)
   attn_fwd_workspace_size(B, H, Sq, Skv, D, ...)          -> bytes
   attn_fwd_split_plan(B, H, Sq, Skv, D, slots, ws_bytes)  -> (split_tiles, pieces, bytes)
   attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None) -> (o_out, lse_out)
@@ -21,10 +22,10 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import (BF16, F16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD, CpattnError, check,
-                   lib)
+from ._lib import (BF16, F16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD, STATIC_SCRATCH_BYTES,
+                   CpattnError, check, lib)
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_static", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge",
            "qk_rmsnorm", "attn_fwd_fp8", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
            "SEQ_TO_HEAD", "HEAD_TO_SEQ", "CpattnError", "lib"]
 
@@ -113,6 +114,24 @@ def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, out_dtype=None, workspace
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     flags = (FLAG_ACCUMULATE if accumulate else 0) | (FLAG_SEQ_MAJOR if seq_major else 0)
     check("cpattn_attn_fwd_ex", lib().cpattn_attn_fwd_ex(*args, flags, ws_ptr, ws_bytes, _stream(stream)))
+    return o, lse
+
+
+def attn_fwd_ex_static(q, k, v, o=None, lse=None, scale=None, out_dtype=None, scratch_bytes=None, accumulate=False,
+                       seq_major=False, stream=None):
+    """attn_fwd_ex with the split workspace taken from the library's static per-device scratch
+    (the library allocates nothing; pass o and lse to allocate nothing here either).
+    scratch_bytes: how much of the scratch the split may use (default: the best plan's size,
+    at most STATIC_SCRATCH_BYTES)."""
+    if accumulate and (o is None or lse is None):
+        raise ValueError("accumulate needs the existing o and lse")
+    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major)
+    if scratch_bytes is None:
+        B, H, Sq, Skv, D = args[5], args[6], args[7], args[8], args[9]
+        scratch_bytes = min(attn_fwd_workspace_size(B, H, Sq, Skv, D, args[11], args[12]), STATIC_SCRATCH_BYTES)
+    flags = (FLAG_ACCUMULATE if accumulate else 0) | (FLAG_SEQ_MAJOR if seq_major else 0)
+    check("cpattn_attn_fwd_ex_static",
+          lib().cpattn_attn_fwd_ex_static(*args, flags, int(scratch_bytes), _stream(stream)))
     return o, lse
 
 

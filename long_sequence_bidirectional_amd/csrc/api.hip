@@ -260,24 +260,52 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd(const void* q, const void* k, const 
                     static_cast<cpattn_dtype>(odt), false, false, nullptr, nullptr, 0, stream);
 }
 
+namespace {
+
+// Checks of attn_fwd_ex other than those of its workspace (flags, tensors, dtypes, layout limits).
+cpattn_status check_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int idt, int odt,
+                                uint32_t flags, AttnFwdCheck* ck) {
+    if ((flags & ~(uint32_t)(CPATTN_FLAG_ACCUMULATE | CPATTN_FLAG_SEQ_MAJOR)) != 0) return CPATTN_E_FLAGS;
+    const bool acc = (flags & CPATTN_FLAG_ACCUMULATE) != 0;
+    const bool seq_major = (flags & CPATTN_FLAG_SEQ_MAJOR) != 0;
+    const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, ck);
+    if (st != CPATTN_OK) return st;
+    if (acc && (!dtype_16bit(idt) || odt != CPATTN_F32)) return CPATTN_E_DTYPE;
+    // the 16-bit kernels address a 64-row K/V block with 32-bit byte offsets
+    if (seq_major && H * D >= (int64_t(1) << 25)) return CPATTN_E_SHAPE;
+    return CPATTN_OK;
+}
+
+// attn_fwd_ex after every check, with a workspace of workspace_bytes at `workspace` (or none).
+cpattn_status run_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                              int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int idt, int odt,
+                              uint32_t flags, void* workspace, uint64_t workspace_bytes, hipStream_t stream) {
+    int64_t ws_pieces = 0;
+    float *ws_o = nullptr, *ws_lse = nullptr;
+    if (workspace && workspace_bytes > 0) {
+        // layout: ws_o [pieces, tile rows, D] then ws_lse [pieces, tile rows]
+        ws_pieces = (int64_t)(workspace_bytes / piece_bytes(D));
+        ws_o = static_cast<float*>(workspace);
+        ws_lse = ws_o + (size_t)ws_pieces * cpattn::kAttnTileRows * D;
+    }
+    return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
+                    static_cast<cpattn_dtype>(odt), (flags & CPATTN_FLAG_ACCUMULATE) != 0,
+                    (flags & CPATTN_FLAG_SEQ_MAJOR) != 0, ws_o, ws_lse, ws_pieces, stream);
+}
+
+}  // namespace
+
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                                                int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                                                float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
                                                uint32_t flags, void* workspace, uint64_t workspace_bytes,
                                                hipStream_t stream) {
-    if ((flags & ~(uint32_t)(CPATTN_FLAG_ACCUMULATE | CPATTN_FLAG_SEQ_MAJOR)) != 0) return CPATTN_E_FLAGS;
-    const bool acc = (flags & CPATTN_FLAG_ACCUMULATE) != 0;
-    const bool seq_major = (flags & CPATTN_FLAG_SEQ_MAJOR) != 0;
     const int idt = enum_bits(in_dtype), odt = enum_bits(o_dtype);
     AttnFwdCheck ck;
-    const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, &ck);
+    const cpattn_status st = check_attn_fwd_ex(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, flags, &ck);
     if (st != CPATTN_OK) return st;
-    if (acc && (!dtype_16bit(idt) || odt != CPATTN_F32)) return CPATTN_E_DTYPE;
-    // the 16-bit kernels address a 64-row K/V block with 32-bit byte offsets
-    if (seq_major && H * D >= (int64_t(1) << 25)) return CPATTN_E_SHAPE;
     if (workspace_bytes != 0 && !workspace) return CPATTN_E_NULL;
-    int64_t ws_pieces = 0;
-    float *ws_o = nullptr, *ws_lse = nullptr;
     if (workspace && workspace_bytes > 0) {
         if (!aligned16(workspace)) return CPATTN_E_ALIGN;
         if (workspace_bytes > (uint64_t)kMaxElems) return CPATTN_E_SHAPE;
@@ -285,13 +313,56 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, con
         if (overlap(rw, ck.rq) || overlap(rw, ck.rk) || overlap(rw, ck.rv) || overlap(rw, ck.ro) ||
             overlap(rw, ck.rl))
             return CPATTN_E_ALIAS;
-        // layout: ws_o [pieces, tile rows, D] then ws_lse [pieces, tile rows]
-        ws_pieces = (int64_t)(workspace_bytes / piece_bytes(D));
-        ws_o = static_cast<float*>(workspace);
-        ws_lse = ws_o + (size_t)ws_pieces * cpattn::kAttnTileRows * D;
     }
-    return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
-                    static_cast<cpattn_dtype>(odt), acc, seq_major, ws_o, ws_lse, ws_pieces, stream);
+    return run_attn_fwd_ex(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, flags, workspace, workspace_bytes,
+                           stream);
+}
+
+// ---- the library's static scratch (cpattn_attn_fwd_ex_static)
+//
+// A file-scope device array: every device the library runs on holds its own copy, at its own
+// address, from the first use on that device until the process ends.  In host code the name is
+// only a handle for hipGetSymbolAddress, never an address: the device address is looked up once
+// per device, with that device current, and only that address reaches kernels.
+static __device__ __align__(256) unsigned char scratch[CPATTN_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device (null if HIP cannot give it), kept per device.
+void* static_scratch_ptr() {
+    constexpr int kCachedDevices = 64;
+    static std::atomic<void*> cache[kCachedDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::atomic<void*>* slot = (dev >= 0 && dev < kCachedDevices) ? &cache[dev] : nullptr;
+    if (slot) {
+        void* p = slot->load(std::memory_order_acquire);
+        if (p) return p;
+    }
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    if (slot) slot->store(ptr, std::memory_order_release);
+    return ptr;
+}
+
+}  // namespace
+
+CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex_static(const void* q, const void* k, const void* v, void* o,
+                                                      float* lse, int64_t B, int64_t H, int64_t Sq, int64_t Skv,
+                                                      int64_t D, float scale, cpattn_dtype in_dtype,
+                                                      cpattn_dtype o_dtype, uint32_t flags, uint64_t scratch_bytes,
+                                                      hipStream_t stream) {
+    const int idt = enum_bits(in_dtype), odt = enum_bits(o_dtype);
+    AttnFwdCheck ck;
+    const cpattn_status st = check_attn_fwd_ex(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, flags, &ck);
+    if (st != CPATTN_OK) return st;
+    if (scratch_bytes > (uint64_t)CPATTN_STATIC_SCRATCH_BYTES) return CPATTN_E_SHAPE;
+    void* ws = nullptr;
+    if (scratch_bytes > 0) {
+        ws = static_scratch_ptr();
+        if (!ws) return CPATTN_E_HIP;
+    }
+    return run_attn_fwd_ex(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, flags, ws, scratch_bytes, stream);
 }
 
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -39,7 +39,7 @@ def header_functions():
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(["cpattn_abi_version", "cpattn_attn_fwd", "cpattn_attn_fwd_ex",
-                                         "cpattn_attn_fwd_fp8",
+                                         "cpattn_attn_fwd_ex_static", "cpattn_attn_fwd_fp8",
                                          "cpattn_attn_fwd_split_plan", "cpattn_attn_fwd_workspace_size",
                                          "cpattn_attn_merge", "cpattn_qk_rmsnorm", "cpattn_ring_attn_fwd",
                                          "cpattn_status_string",
@@ -57,7 +57,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.cpattn_abi_version() == _lib.ABI_VERSION == 2
+    assert L.cpattn_abi_version() == _lib.ABI_VERSION == 3
     seen = set()
     for s in range(10):
         msg = L.cpattn_status_string(s)
@@ -135,6 +135,30 @@ def test_attn_fwd_ex_validation(L):
     assert fwd_ex(L, ws=A + 4096) == _lib.E_ALIAS            # on top of q
     assert fwd_ex(L, ws=D_ - 4096, ws_bytes=8192) == _lib.E_ALIAS   # runs into o
     assert fwd_ex(L, ws=E, ws_bytes=16) == _lib.E_ALIAS      # on top of lse
+
+
+def fwd_static(L, q=A, k=B_, v=C, o=D_, lse=E, B=1, H=2, Sq=256, Skv=256, D=64, scale=0.125, i=0, od=0, flags=0,
+               nbytes=1 << 20):
+    return L.cpattn_attn_fwd_ex_static(q, k, v, o, lse, B, H, Sq, Skv, D, scale, i, od, flags, nbytes, None)
+
+
+def test_attn_fwd_ex_static_validation(L):
+    """Every check of attn_fwd_ex except the workspace pointer's, plus the scratch limit; all of
+    them run before the one HIP call (the lookup of the scratch's device address)."""
+    limit = 32 << 20
+    assert _lib.STATIC_SCRATCH_BYTES == limit
+    m = re.search(r"#define CPATTN_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == limit
+    assert fwd_static(L, nbytes=limit + 1) == _lib.E_SHAPE
+    assert fwd_static(L, nbytes=2 ** 64 - 1) == _lib.E_SHAPE
+    assert fwd_static(L, q=None) == _lib.E_NULL
+    assert fwd_static(L, i=_lib.F32, od=_lib.BF16) == _lib.E_DTYPE
+    assert fwd_static(L, D=96) == _lib.E_HEADDIM
+    assert fwd_static(L, scale=float("nan")) == _lib.E_SCALE
+    assert fwd_static(L, o=A + 16) == _lib.E_ALIAS
+    assert fwd_static(L, flags=4) == _lib.E_FLAGS
+    assert fwd_static(L, flags=_lib.FLAG_ACCUMULATE, od=_lib.BF16) == _lib.E_DTYPE
+    assert fwd_static(L, flags=_lib.FLAG_SEQ_MAJOR, H=1 << 19, Sq=1, Skv=1) == _lib.E_SHAPE
 
 
 def plan(L, B=1, H=24, Sq=44160, Skv=44160, D=128, slots=256, ws=2**64 - 1):
