@@ -146,15 +146,22 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
  *                    bits -> CPATTN_E_FLAGS.
  *
  * Workspace.  The bf16 kernel runs 256 query rows of one (b, h) per
- * workgroup; when the tiles do not fill the device's last wave, the keys of
- * the tiles in that wave are split into pieces that run in parallel, and a
+ * workgroup, at most one workgroup per resident slot, each looping over
+ * units of work.  The first 256 bytes of a workspace hold a work counter:
+ * after the first round, units are claimed from it, so the parts of the
+ * device that run faster (the XCDs' clocks differ under the power limit)
+ * take more of them (the call clears the counter itself, with a kernel).
+ * When the tiles do not fill the device's last wave, the keys of the tiles
+ * in that wave are also split into pieces that run in parallel, and a
  * second kernel folds the pieces with the attn_merge rule.  The split is
  * planned per call from the device's resident-workgroup count and limited
- * to what the workspace holds: (D + 1) * 1024 bytes per piece.
- * cpattn_attn_fwd_workspace_size gives the size the best plan uses;
- * less (or none) only means fewer (or no) pieces.  f32 inputs never split;
- * bf16 and fp16 inputs share the plan.
- * Results differ from cpattn_attn_fwd's only by f32 rounding in the fold.
+ * to what the rest of the workspace holds: (D + 1) * 1024 bytes per piece.
+ * cpattn_attn_fwd_workspace_size gives the size the best plan uses (256
+ * bytes when no split helps); less only means fewer (or no) pieces, and
+ * under 256 bytes (or none) also the static unit order of cpattn_attn_fwd.
+ * f32 inputs never split; bf16 and fp16 inputs share the plan.
+ * Results differ from cpattn_attn_fwd's only by f32 rounding in the fold:
+ * without a split the two give the same bits.
  *
  * CPATTN_FLAG_ACCUMULATE.  (o, lse) hold on entry the result of attention
  * over a disjoint key set (O normalised, f32; LSE natural; LSE = -inf with
@@ -196,8 +203,9 @@ cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, vo
  * check and result is that of cpattn_attn_fwd_ex: with the same
  * scratch_bytes as workspace_bytes the outputs are the same bits.
  *
- * Nothing in the scratch needs clearing between calls: a call writes every
- * byte its piece merge reads before reading it, in stream order.  All calls
+ * Nothing in the scratch needs clearing by the caller: the call clears the
+ * work counter at its head with a kernel of its own (no memset), and writes
+ * every byte its piece merge reads before reading it, in stream order.  All calls
  * on one device share that device's scratch, so calls on one device must not
  * overlap in time (issue them on one stream, or order the streams): two
  * overlapping calls race on it.
@@ -234,7 +242,7 @@ cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, v
 
 /*
  * Workspace bytes cpattn_attn_fwd_ex uses for this problem on the CURRENT
- * device (0 when no split helps, and for f32 inputs).  Makes HIP queries of
+ * device (256 for the work counter when no split helps; 0 for f32 inputs).  Makes HIP queries of
  * the current device (CU count, kernel occupancy); CPATTN_E_HIP if they fail.
  * Shape checks as for cpattn_attn_fwd (the scale is not needed).
  */
@@ -247,7 +255,8 @@ cpattn_status cpattn_attn_fwd_workspace_size(int64_t B, int64_t H, int64_t Sq, i
  * `slots` attention workgroups at once, with workspace_bytes of workspace.
  * Host only, no HIP call.  Outputs: split_tiles = number of trailing query
  * tiles split (0 = no split), pieces = pieces per split tile (1 if none),
- * bytes_used = workspace the plan uses.  slots = 0 means "unknown" (no
+ * bytes_used = workspace the plan uses (the 256-byte work counter plus the
+ * pieces; 0 when workspace_bytes < 256).  slots = 0 means "unknown" (no
  * split).  Shape checks as for cpattn_attn_fwd.
  */
 cpattn_status cpattn_attn_fwd_split_plan(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
@@ -289,8 +298,8 @@ cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_a, const void*
  * Chunk 0's attention is written to (o, lse); every later chunk's attention
  * is folded into (o, lse) in its epilogue with the attn_merge rule (f32), as
  * cpattn_attn_fwd_ex with CPATTN_FLAG_ACCUMULATE does.  The work buffers, when
- * given, serve as the workspace of the key-range split (contents undefined
- * on return).  The result equals attention over the concatenation of all
+ * given, serve as the workspace (the work counter in the first 256 bytes of
+ * lse_work, the key-range pieces in the rest; contents undefined on return).  The result equals attention over the concatenation of all
  * chunks.  n_chunks >= 1, Skv_chunk >= 0, D in {64, 128}, scale as for
  * attn_fwd.  o, lse, o_work and lse_work must not overlap each other or the
  * inputs.

@@ -172,10 +172,11 @@ cpattn::Strides layout_strides(int64_t H, int64_t S, int64_t D, bool seq_major) 
 
 // Attention of one K/V set into (o, lse): written, or folded into them when accumulate.
 // ws_o/ws_lse (capacity ws_pieces pieces each) hold the partials of a split; null = no split.
+// sched (cpattn::kSchedBytes of device memory) enables the dynamic unit schedule; null = static.
 cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                        int64_t Sq, int64_t Skv, int64_t D, float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
                        bool accumulate, bool seq_major, float* ws_o, float* ws_lse, int64_t ws_pieces,
-                       hipStream_t stream) {
+                       unsigned long long* sched, hipStream_t stream) {
     const int64_t BH = B * H;
     if (Skv == 0) {   // empty key set: O = 0, LSE = -inf, the identity of the fold
         if (accumulate) return CPATTN_OK;
@@ -202,8 +203,10 @@ cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, flo
     a.split_tiles = 0;
     a.split_pieces = 1;
     a.slots = 0;
+    a.sched = nullptr;
     a.stream = stream;
     if (in_dtype == CPATTN_F32) return hip_status(cpattn::launch_attn_fwd_f32(a));
+    a.sched = sched;
     a.slots = device_slots(D, a.out_f32);
     if (ws_o && ws_lse && ws_pieces > 0) {
         const SplitPlan p = plan_split(BH, Sq, Skv, D, a.slots, (uint64_t)ws_pieces * piece_bytes(D));
@@ -257,7 +260,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd(const void* q, const void* k, const 
     const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, &ck);
     if (st != CPATTN_OK) return st;
     return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
-                    static_cast<cpattn_dtype>(odt), false, false, nullptr, nullptr, 0, stream);
+                    static_cast<cpattn_dtype>(odt), false, false, nullptr, nullptr, 0, nullptr, stream);
 }
 
 namespace {
@@ -283,15 +286,17 @@ cpattn_status run_attn_fwd_ex(const void* q, const void* k, const void* v, void*
                               uint32_t flags, void* workspace, uint64_t workspace_bytes, hipStream_t stream) {
     int64_t ws_pieces = 0;
     float *ws_o = nullptr, *ws_lse = nullptr;
-    if (workspace && workspace_bytes > 0) {
-        // layout: ws_o [pieces, tile rows, D] then ws_lse [pieces, tile rows]
-        ws_pieces = (int64_t)(workspace_bytes / piece_bytes(D));
-        ws_o = static_cast<float*>(workspace);
+    unsigned long long* sched = nullptr;
+    if (workspace && workspace_bytes >= (uint64_t)cpattn::kSchedBytes) {
+        // layout: schedule counters [kSchedBytes], ws_o [pieces, tile rows, D], ws_lse [pieces, tile rows]
+        sched = static_cast<unsigned long long*>(workspace);
+        ws_pieces = (int64_t)((workspace_bytes - cpattn::kSchedBytes) / piece_bytes(D));
+        ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + cpattn::kSchedBytes);
         ws_lse = ws_o + (size_t)ws_pieces * cpattn::kAttnTileRows * D;
     }
     return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
                     static_cast<cpattn_dtype>(odt), (flags & CPATTN_FLAG_ACCUMULATE) != 0,
-                    (flags & CPATTN_FLAG_SEQ_MAJOR) != 0, ws_o, ws_lse, ws_pieces, stream);
+                    (flags & CPATTN_FLAG_SEQ_MAJOR) != 0, ws_o, ws_lse, ws_pieces, sched, stream);
 }
 
 }  // namespace
@@ -422,10 +427,12 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_split_plan(int64_t B, int64_t H, int
     const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, 1.0f, 32, &c);
     if (st != CPATTN_OK) return st;
     if (slots < 0 || slots > kMaxDim) return CPATTN_E_SHAPE;
-    const SplitPlan p = plan_split(B * H, Sq, Skv, D, slots, workspace_bytes);
+    // the workspace starts with the dynamic schedule's counters; less than that is no workspace
+    const bool sched = workspace_bytes >= (uint64_t)cpattn::kSchedBytes;
+    const SplitPlan p = plan_split(B * H, Sq, Skv, D, slots, sched ? workspace_bytes - cpattn::kSchedBytes : 0);
     *split_tiles = p.split_tiles;
     *pieces = p.pieces;
-    *bytes_used = p.bytes;
+    *bytes_used = sched ? p.bytes + cpattn::kSchedBytes : 0;
     return CPATTN_OK;
 }
 
@@ -442,7 +449,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_workspace_size(int64_t B, int64_t H,
     if (!dtype_16bit(idt)) return CPATTN_OK;
     const int64_t slots = device_slots(D, odt == CPATTN_F32);
     if (slots <= 0) return CPATTN_E_HIP;
-    *bytes = plan_split(B * H, Sq, Skv, D, slots, UINT64_MAX).bytes;
+    *bytes = cpattn::kSchedBytes + plan_split(B * H, Sq, Skv, D, slots, UINT64_MAX).bytes;
     return CPATTN_OK;
 }
 
@@ -503,14 +510,21 @@ CPATTN_EXPORT cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_ch
             if (overlap(outs[i], outs[j])) return CPATTN_E_ALIAS;
     }
     const int64_t chunk_bytes = c.kv_elems * 2;
-    // o_work / lse_work hold the key-range pieces of split tiles (one tile of rows each)
-    const int64_t ws_pieces = (o_work && lse_work) ? c.rows / cpattn::kAttnTileRows : 0;
+    // The work buffers, when given, are the workspace: the dynamic schedule's counters take the
+    // head of lse_work, and the key-range pieces of split tiles (one tile of rows each) take
+    // o_work and the rest of lse_work.
+    constexpr int64_t kSchedFloats = cpattn::kSchedBytes / 4;
+    const bool work = o_work && lse_work && c.rows >= kSchedFloats;
+    unsigned long long* sched = work ? reinterpret_cast<unsigned long long*>(lse_work) : nullptr;
+    const int64_t ws_pieces =
+        work ? std::min(c.rows / cpattn::kAttnTileRows, (c.rows - kSchedFloats) / cpattn::kAttnTileRows) : 0;
+    float* ws_lse = work ? lse_work + kSchedFloats : nullptr;
     cpattn_status s = CPATTN_OK;
     for (int64_t ch = 0; ch < n_chunks && s == CPATTN_OK; ++ch) {
         const char* kc = static_cast<const char*>(k_chunks) + ch * chunk_bytes;
         const char* vc = static_cast<const char*>(v_chunks) + ch * chunk_bytes;
         s = run_attn(q, kc, vc, o, lse, B, H, Sq, Skv_chunk, D, scale, CPATTN_BF16, CPATTN_F32, ch > 0, false,
-                     o_work, lse_work, ws_pieces, stream);
+                     work ? o_work : nullptr, ws_lse, ws_pieces, sched, stream);
     }
     return s;
 }

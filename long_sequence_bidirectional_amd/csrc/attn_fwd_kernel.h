@@ -78,6 +78,7 @@
 // last valid row (finite values that get weight 0 or are never stored).
 #pragma once
 
+#include <climits>
 #include <utility>
 
 #include "common.h"
@@ -133,12 +134,20 @@ __device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
     else return pack_bf16x2(lo, hi);
 }
 
-// One work unit (a whole tile or a key-range piece of one) of a workgroup.
+// One work unit (a whole tile or a key-range piece of one) of a workgroup.  Units are numbered
+// k = 0 .. n_dp - 1 for the whole tiles [0, n_dp) and k = n_dp + p * n_split + ti for piece p
+// of split tile n_dp + ti (piece-major, so that pieces running together read the same keys).
+// A piece p of s covers key blocks [p*nblk/s, (p+1)*nblk/s) and leaves a normalised f32 partial
+// and its LSE in workspace slot ti * s + p.
+//
+// With a dynamic schedule (map.sched) the lane that claims work takes the next unit from the
+// counter right after the block loop, so the atomic's latency overlaps the epilogue; the claim
+// is passed to every wave through *next_lds and returned (-1 without a dynamic schedule).
 template <int D, bool F16, bool OUT_F32, bool SEQ>
-__device__ __forceinline__ void attn_unit(
-    int bid, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+__device__ __forceinline__ int attn_unit(
+    int k_unit, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
-    Strides so, AttnTileMap map, float c) {
+    Strides so, AttnTileMap map, float c, int* next_lds) {
     constexpr int BN = kBN;
     constexpr int NC = D / 8;               // 16-byte chunks per row
     constexpr int NKS = D / 16;             // k-steps of the QK^T product
@@ -155,24 +164,12 @@ __device__ __forceinline__ void attn_unit(
     __shared__ __attribute__((aligned(1024))) uint16_t Ks[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs[NBUF][BN * D];
 
-    // Work unit of this workgroup.  Workgroup ids are dealt round-robin over the
-    // XCDs; both parts of the grid are mapped so that each XCD walks a contiguous
-    // range of units, i.e. the workgroups resident on one XCD share a head and
-    // its K/V stream in L2.  Ids below grid_dp run whole tiles [0, n_dp); the
-    // rest run key-range pieces of tiles [n_dp, n_dp + n_split), piece-major so
-    // that neighbours read the same keys.  A piece p of s covers key blocks
-    // [p*nblk/s, (p+1)*nblk/s) and leaves a normalised f32 partial and its LSE
-    // in workspace slot (tile - n_dp) * s + p.
     const int nblk_all = (Skv_all + BN - 1) / BN;
     int tile, kb0 = 0, slot = -1, nblk = nblk_all;
-    if (bid < map.grid_dp) {
-        const int logical = (bid % kNumXcd) * map.per_xcd_dp + bid / kNumXcd;
-        if (logical >= map.n_dp) return;
-        tile = logical;
+    if (k_unit < map.n_dp) {
+        tile = k_unit;
     } else {
-        const int u = bid - map.grid_dp;
-        const int logical = (u % kNumXcd) * map.per_xcd_sp + u / kNumXcd;
-        if (logical >= map.n_split * map.split_s) return;
+        const int logical = k_unit - map.n_dp;
         const int p = logical / map.n_split;
         const int ti = logical - p * map.n_split;
         tile = map.n_dp + ti;
@@ -514,6 +511,9 @@ __device__ __forceinline__ void attn_unit(
         default: body(ic<3>{}, F{}, T{}, F{}, nblk); break;
     }
     if (group == 0) slot_barrier();
+    unsigned long long claim = 0;
+    if (map.sched != nullptr && tid == 0)
+        claim = __hip_atomic_fetch_add(map.sched, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2; a piece goes to the workspace, an
     // accumulating call folds the result into the (O, LSE) already in o/lse.
@@ -566,20 +566,71 @@ __device__ __forceinline__ void attn_unit(
             }
         if (hh == 0) lse[(size_t)bh * Sq + qrow] = L;
     }
+    if (map.sched == nullptr) return -1;
+    // Every wave read the previous claim before the first barrier of this unit, so the slot
+    // is free; after this barrier every wave sees the new one.
+    if (tid == 0) *next_lds = (int)min(claim, (unsigned long long)INT_MAX - (unsigned long long)gridDim.x);
+    __syncthreads();
+    return *next_lds + (int)gridDim.x;
 }
 
-// At most one workgroup per resident slot, each looping over work units u = blockIdx.x +
-// k * gridDim.x: a finished unit is followed by the next one without a new workgroup launch.
-// gridDim.x is a multiple of the XCD count, so unit u still runs on XCD u % 8, which the unit
-// order above relies on.  A unit's last LDS reads end before its final barrier, so the next
-// unit's loads into the same buffers need no extra synchronisation.
+// At most one workgroup per resident slot (gridDim.x of them, a multiple of the XCD count), each
+// looping over work units, so a finished unit is followed by the next one without a new workgroup
+// launch.  A unit's last LDS reads end before its final barrier, so the next unit's loads into the
+// same buffers need no extra synchronisation.
+//
+// Static schedule (no counter): workgroup b runs b, b + gridDim.x, ... of a grid of units in which
+// ids are dealt round-robin over the XCDs and mapped so that each XCD walks a contiguous range of
+// whole tiles (then of pieces): the workgroups resident on one XCD share a head's K/V stream in
+// its L2.
+//
+// Dynamic schedule (map.sched, zeroed before the launch): the first round is the same XCD-aware
+// map over the first gridDim.x units; every later unit is claimed from the counter in unit order,
+// so XCDs that run faster (their clocks differ under the power limit) take more units, and the
+// workgroups of one XCD, which finish their units together, claim neighbouring tiles together.
+// Every claim advances the counter, so each unit runs once and every workgroup leaves the loop.
 template <int D, bool F16, bool OUT_F32, bool SEQ>
 __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
-    Strides so, AttnTileMap map, float c, int n_units) {
-    for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x)   // 64-bit: no overflow near INT_MAX units
-        attn_unit<D, F16, OUT_F32, SEQ>((int)u, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv, so, map, c);
+    Strides so, AttnTileMap map, float c, int n_grid) {
+    __shared__ int next_unit;
+    const int n_units = map.n_dp + map.n_split * map.split_s;
+    const bool dynamic = map.sched != nullptr;
+    // Unit of static grid id `bid`, or -1 for the padding ids of the XCD-aware map.
+    auto static_unit = [&](int64_t bid) -> int {
+        if (bid < map.grid_dp) {
+            const int u = (int)((bid % kNumXcd) * map.per_xcd_dp + bid / kNumXcd);
+            return u < map.n_dp ? u : -1;
+        }
+        const int64_t w = bid - map.grid_dp;
+        const int logical = (int)((w % kNumXcd) * map.per_xcd_sp + w / kNumXcd);
+        return logical < map.n_split * map.split_s ? map.n_dp + logical : -1;
+    };
+    const int G = (int)gridDim.x;
+    const int b = (int)blockIdx.x;
+    int64_t bid = b;                       // static schedule: next grid id (64-bit: no overflow near INT_MAX)
+    int u;
+    if (dynamic) {
+        u = n_units >= G ? (b % kNumXcd) * (G / kNumXcd) + b / kNumXcd : b;
+    } else {
+        u = -1;
+        for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
+    }
+    while (u >= 0 && u < n_units) {       // one call site: the unit body is inlined once
+        const int claimed =
+            attn_unit<D, F16, OUT_F32, SEQ>(u, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv, so, map, c, &next_unit);
+        if (dynamic) {
+            u = claimed;
+        } else {
+            u = -1;
+            for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
+        }
+    }
+}
+
+__global__ void zero_sched_kernel(unsigned long long* sched) {
+    if (threadIdx.x < kSchedWords) sched[threadIdx.x] = 0;
 }
 
 template <int D, bool F16, bool OUT_F32, bool SEQ>
@@ -596,10 +647,16 @@ hipError_t launch(const AttnFwdArgs& a) {
     m.ws_o = a.ws_o;
     m.ws_lse = a.ws_lse;
     m.accumulate = a.accumulate ? 1 : 0;
-    const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;   // work units (a multiple of kNumXcd)
+    m.sched = a.sched;
+    const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;   // static unit grid (a multiple of kNumXcd)
     const float c = (float)((double)a.scale * 1.4426950408889634);
     const int64_t cap = a.slots - a.slots % kNumXcd;
     const int launch_grid = (cap > 0 && grid > cap) ? (int)cap : grid;
+    if (m.sched != nullptr) {
+        hipLaunchKernelGGL(zero_sched_kernel, dim3(1), dim3(64), 0, a.stream, m.sched);
+        const hipError_t ez = hipGetLastError();
+        if (ez != hipSuccess) return ez;
+    }
     hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, F16, OUT_F32, SEQ>), dim3(launch_grid), dim3(512), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)a.H, a.sq,

@@ -44,8 +44,15 @@ struct AttnFwdArgs {
     // Workgroups of the 16-bit kernel resident at once on the current device (0 = unknown):
     // the kernel is launched with at most that many workgroups, each looping over work units.
     int64_t slots;
+    // Work counter of the dynamic unit schedule (kSchedWords words of device memory, zeroed by
+    // the launcher before the kernel runs), or null for the static schedule.
+    unsigned long long* sched;
     hipStream_t stream;
 };
+
+// Words (and bytes) of the dynamic schedule's counter area at the start of a workspace.
+constexpr int kSchedWords = 32;
+constexpr int kSchedBytes = kSchedWords * 8;
 
 // Kernel-side form of the work split (passed by value).
 struct AttnTileMap {
@@ -54,6 +61,7 @@ struct AttnTileMap {
     float* ws_o;
     float* ws_lse;
     int accumulate;
+    unsigned long long* sched;          // dynamic schedule's counter, or null
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a);

@@ -60,10 +60,15 @@ def test_q_beyond_2_31_elements():
     vb = inputs.random_bf16((1, H, Skv, D), 6102)
     q = dev_bf16(qb).repeat(1, 1, REPEAT, 1)
     n = cp.attn_fwd_workspace_size(1, H, Sq, Skv, D)
-    assert n == 0          # 24 * 4096 tiles fill whole waves: no split
-    o, lse = cp.attn_fwd(q, dev_bf16(kb), dev_bf16(vb))
+    assert n == 256        # 24 * 4096 tiles fill whole waves: no split, only the schedule counters
+    k, v = dev_bf16(kb), dev_bf16(vb)
+    o, lse = cp.attn_fwd(q, k, v)
+    # the dynamic schedule (counters in the workspace) over the same 98304 units: the same bits
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    o2, lse2 = cp.attn_fwd_ex(q, k, v, workspace=ws)
     torch.cuda.synchronize()
-    del q
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(lse2, lse)
+    del q, o2, lse2
     # the last block of rows (offsets up to ~3.2e9 elements) repeats the first bit for bit
     last = slice(Sq - BLOCK, Sq)
     assert torch.equal(o[:, :, last].view(torch.int16), o[:, :, :BLOCK].view(torch.int16))

@@ -66,8 +66,10 @@ def test_workspace_size_bounds_the_split():
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     o_ref, l_ref = cp.attn_fwd(q, k, v)
     piece = 256 * (D + 1) * 4
+    sched = 256           # schedule counters at the head of the workspace
     # no workspace, or room for under two pieces per tile: the unsplit kernel, bit for bit
-    for nbytes in (0, 3 * piece, 15 * piece + 100):
+    # (the dynamic schedule with a workspace runs the same units with the same arithmetic)
+    for nbytes in (0, sched - 1, sched + 3 * piece, sched + 15 * piece + 100):
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         o, l = cp.attn_fwd_ex(q, k, v, workspace=ws)
         torch.cuda.synchronize()
@@ -76,11 +78,31 @@ def test_workspace_size_bounds_the_split():
     # room for 2 or 5 pieces per tile: split, and still correct
     O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
     for pieces in (2, 5):
-        ws = torch.empty(8 * pieces * piece, dtype=torch.uint8, device="cuda")
+        ws = torch.empty(sched + 8 * pieces * piece, dtype=torch.uint8, device="cuda")
         o, l = cp.attn_fwd_ex(q, k, v, workspace=ws)
         torch.cuda.synchronize()
         assert_bf16_parity(host64(o), host64(l), O, L, f"{pieces} pieces per tile")
         assert not same_bits(o, o_ref)
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,D", [(1, 24, 4096, 256, 128),   # 384 tiles, 4 key blocks: no split
+                                          (2, 12, 2600, 300, 64),    # 528 tiles (ragged), D = 64
+                                          (1, 8, 44160, 200, 128)])  # 1384 tiles, 5 per slot
+def test_dynamic_schedule_same_bits(B, H, Sq, Skv, D):
+    """More tiles than resident workgroups and no split: with a workspace the units after the
+    first round are claimed from a counter (dynamic schedule), without one they follow the static
+    map; every unit runs the same arithmetic either way, so the results are the same bits.  The
+    same workspace serves two calls in a row (the launcher clears its counters each time)."""
+    log(f"case: dynamic schedule B{B} H{H} Sq{Sq} Skv{Skv} D{D}")
+    qb, kb, vb = rand_qkv(B, H, Sq, Skv, D, 3150 + Sq)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    ws, n = workspace(B, H, Sq, Skv, D)
+    assert n == 256, "expected the counters only (no split)"
+    o_ref, l_ref = cp.attn_fwd(q, k, v)
+    for rep in range(2):
+        o, l = cp.attn_fwd_ex(q, k, v, workspace=ws)
+        torch.cuda.synchronize()
+        assert same_bits(o, o_ref) and same_bits(l, l_ref), f"call {rep}"
 
 
 def test_whole_tiles_unchanged_by_split():
