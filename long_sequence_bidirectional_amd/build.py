@@ -26,6 +26,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared", "-fvisibility=hidden",
     # No packed-fp32 instructions anywhere in the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The attention kernel's work claim is one lane's atomic whose result is first needed after
+    # the epilogue; the wave-aggregating rewrite would wait for it on the spot.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -535,17 +535,29 @@ __device__ __forceinline__ int attn_unit(
     } else if (qrow < Sq) {
         const int64_t orow = o_base + qrow * o_row;
         float wa = 0.f, wb = inv, L = lse_new;   // O = wa * O_old + wb * acc
-        if (OUT_F32 && map.accumulate) {
-            const float la = lse[(size_t)bh * Sq + qrow];
-            const float mx = fmaxf(la, lse_new);
-            wb = 0.f;
-            L = -INFINITY;
-            if (mx != -INFINITY) {
-                const float ea = expf(la - mx), eb = expf(lse_new - mx);
-                const float tot = ea + eb;
-                L = mx + logf(tot);
-                wa = ea / tot;
-                wb = eb / tot * inv;
+        // Accumulating: every old value this lane folds in is loaded before any store (the stores
+        // go to the same rows, so loads written after them could not be moved ahead of them and
+        // would each wait out a full round trip).
+        f32x4 old[OUT_F32 ? NDT * 4 : 1];
+        if constexpr (OUT_F32) {
+            if (map.accumulate) {
+                const float la = lse[(size_t)bh * Sq + qrow];
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        old[dt * 4 + g] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow +
+                                                                          dt * 32 + g * 8 + hh * 4);
+                const float mx = fmaxf(la, lse_new);
+                wb = 0.f;
+                L = -INFINITY;
+                if (mx != -INFINITY) {
+                    const float ea = expf(la - mx), eb = expf(lse_new - mx);
+                    const float tot = ea + eb;
+                    L = mx + logf(tot);
+                    wa = ea / tot;
+                    wb = eb / tot * inv;
+                }
             }
         }
 #pragma unroll
@@ -556,9 +568,8 @@ __device__ __forceinline__ int attn_unit(
                 f32x4 x = f32x4{oacc[dt][g * 4 + 0], oacc[dt][g * 4 + 1], oacc[dt][g * 4 + 2],
                                 oacc[dt][g * 4 + 3]} * wb;
                 if constexpr (OUT_F32) {
-                    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0);
-                    if (map.accumulate) x += *dst * wa;
-                    *dst = x;
+                    if (map.accumulate) x += old[dt * 4 + g] * wa;
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = x;
                 } else {
                     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + d0) =
                         u32x2{pack16x2<F16>(x[0], x[1]), pack16x2<F16>(x[2], x[3])};
@@ -568,7 +579,9 @@ __device__ __forceinline__ int attn_unit(
     }
     if (map.sched == nullptr) return -1;
     // Every wave read the previous claim before the first barrier of this unit, so the slot
-    // is free; after this barrier every wave sees the new one.
+    // is free; after this barrier every wave sees the new one.  (The claim is first used here,
+    // after the epilogue's stores are issued.)
+    __builtin_amdgcn_sched_barrier(0);
     if (tid == 0) *next_lds = (int)min(claim, (unsigned long long)INT_MAX - (unsigned long long)gridDim.x);
     __syncthreads();
     return *next_lds + (int)gridDim.x;
