@@ -337,8 +337,10 @@ def profile_pass(cp, torch, q, k, v):
                   for _ in range(3))
     o8 = torch.empty((1, H, inputs.S_VIDEO, D), dtype=torch.bfloat16, device="cuda")
     l8 = torch.empty((1, H, inputs.S_VIDEO), dtype=torch.float32, device="cuda")
+    ws8 = torch.empty(cp.attn_fwd_workspace_size(1, H, inputs.S_VIDEO, inputs.S_VIDEO, D, cp.E4M3, cp.BF16),
+                      dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
-    cp.attn_fwd_fp8(q8, k8, v8, o=o8, lse=l8)
+    cp.attn_fwd_fp8(q8, k8, v8, o=o8, lse=l8, workspace=ws8)
     torch.cuda.synchronize()
     del q8, k8, v8, o8, l8
     x = torch.randn((1, inputs.P4_SEQ, inputs.P4_HEADS, D), device="cuda").to(torch.float16)
@@ -551,14 +553,16 @@ PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 matrix-core peak (twice bf16)
 
 def fp8_rows(cp, torch, stream):
     """Self-attention S=44160, H=24, D=128 with E4M3 inputs (N(0,1) draws rounded to E4M3,
-    scales 1) on the fp8 matrix cores; O in bf16.  3 warm-ups, 50 calls timed one by one."""
+    scales 1) on the fp8 matrix cores with its planned workspace; O in bf16.  3 warm-ups, 50 calls timed one by one."""
     from long_sequence_bidirectional_amd import inputs
     S, H, D = inputs.S_VIDEO, inputs.N_HEADS, inputs.HEAD_DIM
     q8, k8, v8 = (torch.from_numpy(inputs.random_e4m3((1, H, S, D), 7300 + i)).cuda() for i in range(3))
     o = torch.empty((1, H, S, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((1, H, S), dtype=torch.float32, device="cuda")
     flops = 4.0 * H * S * S * D
-    leg = timed_leg(torch, stream, lambda: cp.attn_fwd_fp8(q8, k8, v8, o=o, lse=lse, stream=stream), flops)
+    ws = torch.empty(cp.attn_fwd_workspace_size(1, H, S, S, D, cp.E4M3, cp.BF16), dtype=torch.uint8, device="cuda")
+    leg = timed_leg(torch, stream, lambda: cp.attn_fwd_fp8(q8, k8, v8, o=o, lse=lse, workspace=ws, stream=stream),
+                    flops)
     tf = flops / leg["ms_median"] / 1e9
     leg.pop("frac_of_bf16_peak", None)
     leg["frac_of_fp8_peak"] = round(tf / PEAK_FP8_TFLOPS, 4)

@@ -98,7 +98,9 @@ typedef enum {
 #define CPATTN_FLAG_ACCUMULATE 1u
 #define CPATTN_FLAG_SEQ_MAJOR 2u
 
-typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1, CPATTN_F16 = 2 } cpattn_dtype;
+/* CPATTN_E4M3 (OCP FP8 E4M3 bytes) is only an in_dtype of cpattn_attn_fwd_workspace_size:
+ * cpattn_attn_fwd_fp8 takes no dtype for its inputs. */
+typedef enum { CPATTN_BF16 = 0, CPATTN_F32 = 1, CPATTN_F16 = 2, CPATTN_E4M3 = 3 } cpattn_dtype;
 
 typedef enum { CPATTN_SEQ_TO_HEAD = 0, CPATTN_HEAD_TO_SEQ = 1 } cpattn_dir;
 
@@ -231,17 +233,23 @@ cpattn_status cpattn_attn_fwd_ex_static(const void* q, const void* k, const void
  * no recipe; this one runs both products on gfx950's fp8 matrix cores (twice the bf16
  * rate) with f32 scores and softmax state, and rounds the softmax weights to E4M3 (as
  * p * 2^7, p <= 2) for the PV product.  D = 128 only (CPATTN_E_HEADDIM); scales finite
- * and > 0 (CPATTN_E_SCALE); flags: 0 or CPATTN_FLAG_SEQ_MAJOR (else CPATTN_E_FLAGS;
- * sequence-major needs H * D < 2^25, else CPATTN_E_SHAPE);
- * Skv = 0 gives O = 0, LSE = -inf.  Other checks as for cpattn_attn_fwd.
+ * and > 0 (CPATTN_E_SCALE); flags: any of CPATTN_FLAG_SEQ_MAJOR and
+ * CPATTN_FLAG_ACCUMULATE (else CPATTN_E_FLAGS; sequence-major needs H * D < 2^25,
+ * else CPATTN_E_SHAPE; accumulate, as for cpattn_attn_fwd_ex, needs o_dtype = F32,
+ * else CPATTN_E_DTYPE).  workspace / workspace_bytes as for cpattn_attn_fwd_ex (work
+ * counter, then key-range pieces); cpattn_attn_fwd_workspace_size with in_dtype =
+ * CPATTN_E4M3 gives the best plan's size.  Skv = 0 gives O = 0, LSE = -inf (or leaves
+ * an accumulated result unchanged).  Other checks as for cpattn_attn_fwd.
  */
 cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                                   int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale,
                                   float q_scale, float k_scale, float v_scale, cpattn_dtype o_dtype,
-                                  uint32_t flags, hipStream_t stream);
+                                  uint32_t flags, void* workspace, uint64_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
- * Workspace bytes cpattn_attn_fwd_ex uses for this problem on the CURRENT
+ * Workspace bytes cpattn_attn_fwd_ex (in_dtype BF16 or F16) or cpattn_attn_fwd_fp8
+ * (in_dtype E4M3, o_dtype BF16 or F32, D = 128) uses for this problem on the CURRENT
  * device (256 for the work counter when no split helps; 0 for f32 inputs).  Makes HIP queries of
  * the current device (CU count, kernel occupancy); CPATTN_E_HIP if they fail.
  * Shape checks as for cpattn_attn_fwd (the scale is not needed).

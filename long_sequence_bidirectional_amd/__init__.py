@@ -22,7 +22,7 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import (BF16, F16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD, STATIC_SCRATCH_BYTES,
+from ._lib import (BF16, E4M3, F16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD, STATIC_SCRATCH_BYTES,
                    CpattnError, check, lib)
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_static", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge",
@@ -136,9 +136,11 @@ def attn_fwd_ex_static(q, k, v, o=None, lse=None, scale=None, out_dtype=None, sc
 
 
 def attn_fwd_fp8(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, o=None, lse=None, scale=None,
-                 out_dtype=None, seq_major=False, stream=None):
+                 out_dtype=None, seq_major=False, workspace=None, accumulate=False, stream=None):
     """Attention of E4M3 inputs (uint8 codes or torch.float8_e4m3fn) with per-tensor scales;
-    O in bf16 (default) or f32.  Shapes as attn_fwd_ex (head- or sequence-major), D = 128."""
+    O in bf16 (default) or f32.  Shapes as attn_fwd_ex (head- or sequence-major), D = 128;
+    workspace (uint8 device tensor, size from attn_fwd_workspace_size(..., in_dtype=E4M3)) and
+    accumulate (f32 O) as for attn_fwd_ex."""
     torch = _torch()
     for t in (q, k, v):
         if t.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
@@ -161,12 +163,18 @@ def attn_fwd_fp8(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, o=None, lse=Non
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if tuple(o.shape) != o_shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
         raise ValueError(f"o must be {o_shape} and lse float32 [B,H,Sq]")
-    flags = FLAG_SEQ_MAJOR if seq_major else 0
+    if accumulate and (o is None or lse is None):
+        raise ValueError("accumulate needs the existing o and lse")
+    flags = (FLAG_SEQ_MAJOR if seq_major else 0) | (FLAG_ACCUMULATE if accumulate else 0)
     dv = q.device
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None and workspace.numel() > 0:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace", dv), workspace.numel() * workspace.element_size()
     st = lib().cpattn_attn_fwd_fp8(_dev(q, "q"), _dev(k, "k", dv) if Skv else None,
                                    _dev(v, "v", dv) if Skv else None, _dev(o, "o", dv), _dev(lse, "lse", dv),
                                    B, H, Sq, Skv, D, float(scale), float(q_scale),
-                                   float(k_scale), float(v_scale), _dtype_code(o), flags, _stream(stream))
+                                   float(k_scale), float(v_scale), _dtype_code(o), flags, ws_ptr, ws_bytes,
+                                   _stream(stream))
     check("cpattn_attn_fwd_fp8", st)
     return o, lse
 

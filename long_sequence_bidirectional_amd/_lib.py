@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libcpattn.so")
 
 # enum values of include/cpattn.h
 OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_ALIGN, E_ALIAS, E_HIP, E_SCALE, E_FLAGS = range(10)
-BF16, F32, F16 = 0, 1, 2
+BF16, F32, F16, E4M3 = 0, 1, 2, 3
 SEQ_TO_HEAD, HEAD_TO_SEQ = 0, 1
 ABI_VERSION = 3
 STATIC_SCRATCH_BYTES = 32 << 20     # CPATTN_STATIC_SCRATCH_BYTES
@@ -32,7 +32,8 @@ SIGNATURES = [
     ("cpattn_attn_fwd", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _P]),
     ("cpattn_attn_fwd_ex", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _U32, _P, _U64, _P]),
     ("cpattn_attn_fwd_ex_static", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _U32, _U64, _P]),
-    ("cpattn_attn_fwd_fp8", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _F, _F, _F, _E, _U32, _P]),
+    ("cpattn_attn_fwd_fp8", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _F, _F, _F, _E, _U32, _P, _U64,
+                                 _P]),
     ("cpattn_attn_fwd_workspace_size", _E, [_I64, _I64, _I64, _I64, _I64, _E, _E, _PU64]),
     ("cpattn_attn_fwd_split_plan", _E, [_I64, _I64, _I64, _I64, _I64, _I64, _U64, _PI64, _PI64, _PU64]),
     ("cpattn_attn_merge", _E, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _E, _P]),

@@ -145,21 +145,22 @@ SplitPlan plan_split(int64_t BH, int64_t Sq, int64_t Skv, int64_t D, int64_t slo
     return p;
 }
 
-// Workgroups of the bf16 kernel resident at once on the current device (0 if unknown),
-// cached per device and output type.
-int64_t device_slots(int64_t D, bool out_f32) {
+// Workgroups of an attention kernel resident at once on the current device (0 if unknown),
+// cached per device, kernel (16-bit D = 64, D = 128, fp8) and output type.
+int64_t device_slots(int64_t D, bool out_f32, bool fp8 = false) {
     constexpr int kCachedDevices = 64;
-    static std::atomic<int64_t> cache[kCachedDevices][2][2];
+    static std::atomic<int64_t> cache[kCachedDevices][3][2];
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    std::atomic<int64_t>* slot =
-        (dev >= 0 && dev < kCachedDevices) ? &cache[dev][D == 128 ? 1 : 0][out_f32 ? 1 : 0] : nullptr;
+    const int kind = fp8 ? 2 : (D == 128 ? 1 : 0);
+    std::atomic<int64_t>* slot = (dev >= 0 && dev < kCachedDevices) ? &cache[dev][kind][out_f32 ? 1 : 0] : nullptr;
     if (slot) {
         const int64_t v = slot->load(std::memory_order_relaxed);
         if (v > 0) return v;
     }
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    const int64_t v = (int64_t)cus * cpattn::attn_fwd_bf16_blocks_per_cu(D, out_f32);
+    const int64_t v = (int64_t)cus * (fp8 ? cpattn::attn_fwd_fp8_blocks_per_cu(out_f32)
+                                          : cpattn::attn_fwd_bf16_blocks_per_cu(D, out_f32));
     if (slot && v > 0) slot->store(v, std::memory_order_relaxed);
     return v;
 }
@@ -373,12 +374,15 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_ex_static(const void* q, const void*
 CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                                                 int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,
                                                 float scale, float q_scale, float k_scale, float v_scale,
-                                                cpattn_dtype o_dtype, uint32_t flags, hipStream_t stream) {
-    if ((flags & ~(uint32_t)CPATTN_FLAG_SEQ_MAJOR) != 0) return CPATTN_E_FLAGS;
+                                                cpattn_dtype o_dtype, uint32_t flags, void* workspace,
+                                                uint64_t workspace_bytes, hipStream_t stream) {
+    if ((flags & ~(uint32_t)(CPATTN_FLAG_SEQ_MAJOR | CPATTN_FLAG_ACCUMULATE)) != 0) return CPATTN_E_FLAGS;
     const bool seq_major = (flags & CPATTN_FLAG_SEQ_MAJOR) != 0;
+    const bool acc = (flags & CPATTN_FLAG_ACCUMULATE) != 0;
     if (!q || !o || !lse || (Skv != 0 && (!k || !v))) return CPATTN_E_NULL;
     const int odt = enum_bits(o_dtype);
     if (odt != CPATTN_BF16 && odt != CPATTN_F32) return CPATTN_E_DTYPE;
+    if (acc && odt != CPATTN_F32) return CPATTN_E_DTYPE;
     AttnCheck c;
     cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, scale, 32, &c);
     if (st != CPATTN_OK) return st;
@@ -394,7 +398,18 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, co
     if (overlap(ro, rl) || overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) ||
         overlap(rl, rk) || overlap(rl, rv))
         return CPATTN_E_ALIAS;
-    if (Skv == 0) return hip_status(cpattn::launch_fill_empty(o, c.q_elems * osz, lse, c.rows, stream));
+    if (workspace_bytes != 0 && !workspace) return CPATTN_E_NULL;
+    if (workspace && workspace_bytes > 0) {
+        if (!aligned16(workspace)) return CPATTN_E_ALIGN;
+        if (workspace_bytes > (uint64_t)kMaxElems) return CPATTN_E_SHAPE;
+        const Range rw = range(workspace, (int64_t)workspace_bytes);
+        if (overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv) || overlap(rw, ro) || overlap(rw, rl))
+            return CPATTN_E_ALIAS;
+    }
+    if (Skv == 0) {   // empty key set: O = 0, LSE = -inf, the identity of the fold
+        if (acc) return CPATTN_OK;
+        return hip_status(cpattn::launch_fill_empty(o, c.q_elems * osz, lse, c.rows, stream));
+    }
     cpattn::AttnFp8Args a{};
     a.q = q;
     a.k = k;
@@ -414,7 +429,24 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, co
     a.k_scale = k_scale;
     a.v_scale = v_scale;
     a.out_f32 = odt == CPATTN_F32;
+    a.accumulate = acc;
+    a.split_tiles = 0;
+    a.split_pieces = 1;
+    a.slots = device_slots(D, a.out_f32, true);
+    a.sched = nullptr;
     a.stream = stream;
+    if (workspace && workspace_bytes >= (uint64_t)cpattn::kSchedBytes) {
+        // same layout as attn_fwd_ex: counters, then the pieces' O, then their LSE
+        a.sched = static_cast<unsigned long long*>(workspace);
+        const int64_t ws_pieces = (int64_t)((workspace_bytes - cpattn::kSchedBytes) / piece_bytes(D));
+        const SplitPlan p = plan_split(a.BH, Sq, Skv, D, a.slots, (uint64_t)ws_pieces * piece_bytes(D));
+        if (p.split_tiles > 0) {
+            a.split_tiles = p.split_tiles;
+            a.split_pieces = p.pieces;
+            a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + cpattn::kSchedBytes);
+            a.ws_lse = a.ws_o + (size_t)ws_pieces * cpattn::kAttnTileRows * D;
+        }
+    }
     return hip_status(cpattn::launch_attn_fwd_fp8(a));
 }
 
@@ -441,13 +473,16 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_workspace_size(int64_t B, int64_t H,
                                                            uint64_t* bytes) {
     if (!bytes) return CPATTN_E_NULL;
     const int idt = enum_bits(in_dtype), odt = enum_bits(o_dtype);
-    if (!dtype_valid(idt) || !dtype_valid(odt)) return CPATTN_E_DTYPE;
+    const bool fp8 = idt == CPATTN_E4M3;
+    if ((!dtype_valid(idt) && !fp8) || !dtype_valid(odt)) return CPATTN_E_DTYPE;
+    if (fp8 && odt != CPATTN_BF16 && odt != CPATTN_F32) return CPATTN_E_DTYPE;
     AttnCheck c;
     const cpattn_status st = check_attn_shapes(B, H, Sq, Skv, D, 1.0f, 32, &c);
     if (st != CPATTN_OK) return st;
+    if (fp8 && D != 128) return CPATTN_E_HEADDIM;
     *bytes = 0;
-    if (!dtype_16bit(idt)) return CPATTN_OK;
-    const int64_t slots = device_slots(D, odt == CPATTN_F32);
+    if (!dtype_16bit(idt) && !fp8) return CPATTN_OK;
+    const int64_t slots = device_slots(D, odt == CPATTN_F32, fp8);
     if (slots <= 0) return CPATTN_E_HIP;
     *bytes = cpattn::kSchedBytes + plan_split(B * H, Sq, Skv, D, slots, UINT64_MAX).bytes;
     return CPATTN_OK;

@@ -38,6 +38,7 @@
 // weights stay in E4M3's normal range), computed directly as exp2(t - m + 7); the row
 // sum l' of these unrounded f32 values carries the same 2^7, so O = sum(p8 v) * v_scale
 // / l' and LSE = (m + log2 l' - 7) * ln 2.
+#include <climits>
 #include <utility>
 
 #include "common.h"
@@ -86,12 +87,15 @@ __device__ __forceinline__ int pack_fp8x2(float a, float b, int old) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
+// One work unit of a workgroup: a whole query tile k_unit < map.n_dp, or a key-range piece
+// (numbering, piece bounds and the dynamic-schedule claim as in the 16-bit kernel: a piece leaves
+// its normalised f32 O and natural LSE in the workspace for the piece merge).
 template <bool OUT_F32, bool SEQ>
-__global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-                                                           const uint8_t* __restrict__ v, void* __restrict__ o,
-                                                           float* __restrict__ lse, int Sq, int Skv, int nQt, int H,
-                                                           Strides sq, Strides skv, Strides so, int total,
-                                                           int per_xcd, float c, float v_scale) {
+__device__ __forceinline__ int attn_unit_fp8(int k_unit, const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+                                             const uint8_t* __restrict__ v, void* __restrict__ o,
+                                             float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq,
+                                             Strides skv, Strides so, AttnTileMap map, float c, float v_scale,
+                                             int* next_lds) {
     constexpr int D = kD, BN = kBN;
     constexpr int NKS = D / 64;            // k-steps of QK (64 d each)
     constexpr int NDT = D / 32;            // 32-wide d tiles of O^T
@@ -101,11 +105,22 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     __shared__ __attribute__((aligned(1024))) uint8_t Ks[kNBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) uint8_t Vs[kNBUF][BN * D];
 
-    const int bid = blockIdx.x;
-    const int logical = (bid % kNumXcd) * per_xcd + bid / kNumXcd;
-    if (logical >= total) return;
-    const int bh = logical / nQt;
-    const int qt = logical - bh * nQt;
+    const int nblk_all = (Skv_all + BN - 1) / BN;
+    int tile, kb0 = 0, slot = -1, nblk = nblk_all;
+    if (k_unit < map.n_dp) {
+        tile = k_unit;
+    } else {
+        const int logical = k_unit - map.n_dp;
+        const int p = logical / map.n_split;
+        const int ti = logical - p * map.n_split;
+        tile = map.n_dp + ti;
+        slot = ti * map.split_s + p;
+        kb0 = (int)((int64_t)p * nblk_all / map.split_s);
+        nblk = (int)((int64_t)(p + 1) * nblk_all / map.split_s) - kb0;
+    }
+    const int Skv = min(Skv_all - kb0 * BN, nblk * BN);   // keys of this unit
+    const int bh = tile / nQt;
+    const int qt = tile - bh * nQt;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,12 +133,13 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
 
     const int64_t q_row = SEQ ? sq.row : D, kv_row = SEQ ? skv.row : D, o_row = SEQ ? so.row : D;
     const int b = SEQ ? bh / H : 0, h = SEQ ? bh - b * H : 0;
+    const int64_t kv_off =
+        (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv_all * D) + (int64_t)kb0 * BN * kv_row;
     const uint8_t* qp = q + (SEQ ? b * sq.batch + h * sq.head : (int64_t)bh * Sq * D);
-    const uint8_t* kp = k + (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv * D);
-    const uint8_t* vp = v + (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv * D);
+    const uint8_t* kp = k + kv_off;
+    const uint8_t* vp = v + kv_off;
     const int64_t o_base = SEQ ? b * so.batch + h * so.head : (int64_t)bh * Sq * D;
     const int qrow = qt * kBM + wave * 32 + l32;
-    const int nblk = (Skv + BN - 1) / BN;
 
     // One 1 KB piece per wave per tensor: LDS rows 8*wave .. 8*wave+7 of the block.  A load is
     // the block's wave-uniform base (SGPRs) plus a per-lane byte offset that is the same for
@@ -396,41 +412,165 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
         default: body(ic<3>{}, F{}, T{}, nblk); break;
     }
     if (group == 0) slot_barrier();
+    unsigned long long claim = 0;
+    if (map.sched != nullptr && tid == 0)
+        claim = __hip_atomic_fetch_add(map.sched, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+    // epilogue: l carries the 2^7 of the weights; O = acc * v_scale / l, LSE natural
     const float l_tot = sum_across_halves(l_run);
-    if (qrow < Sq) {
-        const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;       // l carries the 2^7 of the weights
-        const int64_t orow = o_base + qrow * o_row;
+    const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
+    const float lse_new = l_tot > 0.f ? (m_run + log2f(l_tot) - kPScaleLog2) * kLn2 : -INFINITY;
+    if (slot >= 0) {
+        const size_t wrow = (size_t)slot * kBM + wave * 32 + l32;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d0 = dt * 32 + g * 8 + hh * 4;
-                const float x0 = oacc[dt][g * 4 + 0] * inv, x1 = oacc[dt][g * 4 + 1] * inv;
-                const float x2 = oacc[dt][g * 4 + 2] * inv, x3 = oacc[dt][g * 4 + 3] * inv;
-                if constexpr (OUT_F32)
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = f32x4{x0, x1, x2, x3};
-                else
-                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + d0) =
-                        u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+                *reinterpret_cast<f32x4*>(map.ws_o + wrow * D + d0) =
+                    f32x4{oacc[dt][g * 4 + 0] * inv, oacc[dt][g * 4 + 1] * inv, oacc[dt][g * 4 + 2] * inv,
+                          oacc[dt][g * 4 + 3] * inv};
             }
-        if (hh == 0)
-            lse[(int64_t)bh * Sq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot) - kPScaleLog2) * kLn2 : -INFINITY;
+        if (hh == 0) map.ws_lse[wrow] = lse_new;
+    } else if (qrow < Sq) {
+        const int64_t orow = o_base + qrow * o_row;
+        float wa = 0.f, wb = inv, L = lse_new;   // O = wa * O_old + wb * acc
+        // accumulating: every old value is loaded before the first store to the same row
+        f32x4 old[OUT_F32 ? NDT * 4 : 1];
+        if constexpr (OUT_F32) {
+            if (map.accumulate) {
+                const float la = lse[(size_t)bh * Sq + qrow];
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        old[dt * 4 + g] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow +
+                                                                          dt * 32 + g * 8 + hh * 4);
+                const float mx = fmaxf(la, lse_new);
+                wb = 0.f;
+                L = -INFINITY;
+                if (mx != -INFINITY) {
+                    const float ea = expf(la - mx), eb = expf(lse_new - mx);
+                    const float tot = ea + eb;
+                    L = mx + logf(tot);
+                    wa = ea / tot;
+                    wb = eb / tot * inv;
+                }
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + g * 8 + hh * 4;
+                f32x4 x = f32x4{oacc[dt][g * 4 + 0], oacc[dt][g * 4 + 1], oacc[dt][g * 4 + 2],
+                                oacc[dt][g * 4 + 3]} * wb;
+                if constexpr (OUT_F32) {
+                    if (map.accumulate) x += old[dt * 4 + g] * wa;
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = x;
+                } else {
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + d0) =
+                        u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                }
+            }
+        if (hh == 0) lse[(size_t)bh * Sq + qrow] = L;
     }
+    if (map.sched == nullptr) return -1;
+    // the claim is first used here, after the epilogue's stores are issued; every wave read the
+    // previous one before the first barrier of this unit
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid == 0) *next_lds = (int)min(claim, (unsigned long long)INT_MAX - (unsigned long long)gridDim.x);
+    __syncthreads();
+    return *next_lds + (int)gridDim.x;
+}
+
+// Persistent workgroups over work units, with the static or the dynamic schedule of the 16-bit
+// kernel (see attn_fwd_kernel.h: the first round XCD-aware, later units from the counter).
+template <bool OUT_F32, bool SEQ>
+__global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+                                                           const uint8_t* __restrict__ v, void* __restrict__ o,
+                                                           float* __restrict__ lse, int Sq, int Skv, int nQt, int H,
+                                                           Strides sq, Strides skv, Strides so, AttnTileMap map,
+                                                           float c, float v_scale, int n_grid) {
+    __shared__ int next_unit;
+    const int n_units = map.n_dp + map.n_split * map.split_s;
+    const bool dynamic = map.sched != nullptr;
+    auto static_unit = [&](int64_t bid) -> int {
+        if (bid < map.grid_dp) {
+            const int u = (int)((bid % kNumXcd) * map.per_xcd_dp + bid / kNumXcd);
+            return u < map.n_dp ? u : -1;
+        }
+        const int64_t w = bid - map.grid_dp;
+        const int logical = (int)((w % kNumXcd) * map.per_xcd_sp + w / kNumXcd);
+        return logical < map.n_split * map.split_s ? map.n_dp + logical : -1;
+    };
+    const int G = (int)gridDim.x;
+    const int bb = (int)blockIdx.x;
+    int64_t bid = bb;
+    int u;
+    if (dynamic) {
+        u = n_units >= G ? (bb % kNumXcd) * (G / kNumXcd) + bb / kNumXcd : bb;
+    } else {
+        u = -1;
+        for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
+    }
+    while (u >= 0 && u < n_units) {       // one call site: the unit body is inlined once
+        const int claimed =
+            attn_unit_fp8<OUT_F32, SEQ>(u, q, k, v, o, lse, Sq, Skv, nQt, H, sq, skv, so, map, c, v_scale, &next_unit);
+        if (dynamic) {
+            u = claimed;
+        } else {
+            u = -1;
+            for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
+        }
+    }
+}
+
+__global__ void zero_sched_kernel_fp8(unsigned long long* sched) {
+    if (threadIdx.x < kSchedWords) sched[threadIdx.x] = 0;
 }
 
 template <bool OUT_F32, bool SEQ>
 hipError_t launch_fp8_typed(const AttnFp8Args& a) {
     const int nQt = (int)((a.Sq + kBM - 1) / kBM);
     const int64_t total = a.BH * nQt;
-    const int per_xcd = (int)((total + kNumXcd - 1) / kNumXcd);
+    AttnTileMap m{};
+    m.n_dp = (int)(total - a.split_tiles);
+    m.per_xcd_dp = (m.n_dp + kNumXcd - 1) / kNumXcd;
+    m.grid_dp = m.per_xcd_dp * kNumXcd;
+    m.n_split = (int)a.split_tiles;
+    m.split_s = a.split_tiles > 0 ? (int)a.split_pieces : 1;
+    m.per_xcd_sp = (m.n_split * m.split_s + kNumXcd - 1) / kNumXcd;
+    m.ws_o = a.ws_o;
+    m.ws_lse = a.ws_lse;
+    m.accumulate = a.accumulate ? 1 : 0;
+    m.sched = a.sched;
+    const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;   // static unit grid (a multiple of kNumXcd)
     const float c = (float)((double)a.scale * 1.4426950408889634 * (double)a.q_scale * (double)a.k_scale);
-
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32, SEQ>), dim3(per_xcd * kNumXcd), dim3(512), 0, a.stream,
+    const int64_t cap = a.slots - a.slots % kNumXcd;
+    const int launch_grid = (cap > 0 && grid > cap) ? (int)cap : grid;
+    if (m.sched != nullptr) {
+        hipLaunchKernelGGL(zero_sched_kernel_fp8, dim3(1), dim3(64), 0, a.stream, m.sched);
+        const hipError_t ez = hipGetLastError();
+        if (ez != hipSuccess) return ez;
+    }
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<OUT_F32, SEQ>), dim3(launch_grid), dim3(512), 0, a.stream,
                        static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
                        static_cast<const uint8_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)a.H, a.sq,
-                       a.skv, a.so, (int)total, per_xcd, c, a.v_scale);
-    return hipGetLastError();
+                       a.skv, a.so, m, c, a.v_scale, grid);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.split_tiles == 0) return e;
+    MergePiecesArgs f{a.ws_o, a.ws_lse, a.o, a.lse, m.n_dp, m.n_split, m.split_s, nQt, a.H, a.so, a.Sq, kD,
+                      OUT_F32 ? MergeOut::F32 : MergeOut::BF16, a.accumulate, a.stream};
+    return launch_merge_pieces(f);
+}
+
+template <bool OUT_F32>
+int occupancy_fp8() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_fp8_kernel<OUT_F32, false>, 512, 0) != hipSuccess)
+        return 0;
+    return n;
 }
 
 }  // namespace
@@ -439,5 +579,7 @@ hipError_t launch_attn_fwd_fp8(const AttnFp8Args& a) {
     if (a.seq_major) return a.out_f32 ? launch_fp8_typed<true, true>(a) : launch_fp8_typed<false, true>(a);
     return a.out_f32 ? launch_fp8_typed<true, false>(a) : launch_fp8_typed<false, false>(a);
 }
+
+int attn_fwd_fp8_blocks_per_cu(bool out_f32) { return out_f32 ? occupancy_fp8<true>() : occupancy_fp8<false>(); }
 
 }  // namespace cpattn

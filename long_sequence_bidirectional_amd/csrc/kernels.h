@@ -68,7 +68,8 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f16(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a);
 
-// Attention with OCP FP8 E4M3 inputs (D = 128), one f32 scale per tensor.
+// Attention with OCP FP8 E4M3 inputs (D = 128), one f32 scale per tensor.  Work split,
+// split pieces, accumulation and schedule as in AttnFwdArgs.
 struct AttnFp8Args {
     const void* q;
     const void* k;
@@ -80,10 +81,20 @@ struct AttnFp8Args {
     Strides sq, skv, so;
     float scale, q_scale, k_scale, v_scale;
     bool out_f32;            // O in f32 (else bf16)
+    bool accumulate;         // fold into the (O, LSE) already in o/lse (out_f32 only)
+    int64_t split_tiles;
+    int64_t split_pieces;
+    float* ws_o;
+    float* ws_lse;
+    int64_t slots;
+    unsigned long long* sched;
     hipStream_t stream;
 };
 
 hipError_t launch_attn_fwd_fp8(const AttnFp8Args& a);
+
+// Resident workgroups per CU of the fp8 attention kernel (0 if the runtime cannot tell).
+int attn_fwd_fp8_blocks_per_cu(bool out_f32);
 
 // Resident workgroups per CU of the bf16 attention kernel (0 if the runtime cannot tell).
 int attn_fwd_bf16_blocks_per_cu(int64_t D, bool out_f32);

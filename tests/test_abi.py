@@ -221,6 +221,11 @@ def test_split_plan_validation(L):
     assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 128, 0, 0, None) == _lib.E_NULL
     assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 128, 7, 0, ctypes.byref(n)) == _lib.E_DTYPE
     assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 48, 0, 0, ctypes.byref(n)) == _lib.E_HEADDIM
+    # E4M3 inputs: D = 128 and a BF16 or F32 O only
+    assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 64, _lib.E4M3, 0, ctypes.byref(n)) == _lib.E_HEADDIM
+    assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 128, _lib.E4M3, _lib.F16, ctypes.byref(n)) == \
+        _lib.E_DTYPE
+    assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 128, 4, 0, ctypes.byref(n)) == _lib.E_DTYPE
     # f32 inputs never split: answered without asking the device
     assert L.cpattn_attn_fwd_workspace_size(1, 2, 100, 100, 128, 1, 1, ctypes.byref(n)) == _lib.OK
     assert n.value == 0
@@ -293,8 +298,8 @@ def test_ring_validation(L):
 
 
 def fp8(L, q=A, k=B_, v=C, o=D_, lse=E, B=1, H=2, Sq=256, Skv=256, D=128, scale=0.1, qs=1.0, ks=1.0, vs=1.0,
-        od=0, flags=0):
-    return L.cpattn_attn_fwd_fp8(q, k, v, o, lse, B, H, Sq, Skv, D, scale, qs, ks, vs, od, flags, None)
+        od=0, flags=0, ws=None, ws_bytes=0):
+    return L.cpattn_attn_fwd_fp8(q, k, v, o, lse, B, H, Sq, Skv, D, scale, qs, ks, vs, od, flags, ws, ws_bytes, None)
 
 
 def test_attn_fwd_fp8_validation(L):
@@ -307,8 +312,14 @@ def test_attn_fwd_fp8_validation(L):
     assert fp8(L, scale=0.0) == _lib.E_SCALE
     assert fp8(L, qs=0.0) == _lib.E_SCALE
     assert fp8(L, vs=float("inf")) == _lib.E_SCALE
-    assert fp8(L, flags=_lib.FLAG_ACCUMULATE) == _lib.E_FLAGS
     assert fp8(L, flags=4) == _lib.E_FLAGS
+    assert fp8(L, flags=_lib.FLAG_ACCUMULATE | 8) == _lib.E_FLAGS
+    assert fp8(L, flags=_lib.FLAG_ACCUMULATE, od=_lib.BF16) == _lib.E_DTYPE     # accumulate needs an f32 O
+    # workspace checks as for attn_fwd_ex
+    assert fp8(L, ws=None, ws_bytes=1024) == _lib.E_NULL
+    assert fp8(L, ws=W + 8, ws_bytes=1024) == _lib.E_ALIGN
+    assert fp8(L, ws=A + 4096, ws_bytes=1024) == _lib.E_ALIAS             # on top of q
+    assert fp8(L, ws=E, ws_bytes=16) == _lib.E_ALIAS                       # on top of lse
     # a token row of H * D >= 2^25 bytes does not fit the kernel's 32-bit block offsets
     assert fp8(L, flags=_lib.FLAG_SEQ_MAJOR, H=1 << 18, Sq=1, Skv=1) == _lib.E_SHAPE
     assert fp8(L, o=E + 16) == _lib.E_ALIGN or fp8(L, o=E + 16) == _lib.E_ALIAS

@@ -127,3 +127,71 @@ def test_fp8_video_self_attention_sampled():
                         o[:, h:h + 1], lse[:, h:h + 1], f"fp8 S=44160 head {h}", rows=rows)
         # at this length the bf16 gates hold as well
         assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def ws_fp8(B, H, Sq, Skv, D, out_f32):
+    n = cp.attn_fwd_workspace_size(B, H, Sq, Skv, D, cp.E4M3, cp.F32 if out_f32 else cp.BF16)
+    return torch.empty(n, dtype=torch.uint8, device="cuda"), n
+
+
+@pytest.mark.parametrize("seq_major", [False, True], ids=["bhsd", "bshd"])
+@pytest.mark.parametrize("out_f32", [False, True], ids=["o_bf16", "o_f32"])
+@pytest.mark.parametrize("B,H,Sq,Skv,D", [(1, 2, 1000, 3000, 128), (1, 3, 513, 700, 128), (1, 1, 17, 2992, 128)])
+def test_fp8_split(B, H, Sq, Skv, D, out_f32, seq_major):
+    """With a workspace the last wave's tiles are cut into key-range pieces (each a normalised
+    f32 partial with its LSE) and folded by the piece merge; units after the first round come
+    from the work counter.  Same derived bound as the unsplit call."""
+    log(f"case: fp8 split B{B} H{H} Sq{Sq} Skv{Skv} out_f32={out_f32} seq_major={seq_major}")
+    seed = 7400 + Sq + Skv
+    q8, k8, v8 = (inputs.random_e4m3(s, seed + i) for i, s in enumerate([(B, H, Sq, D), (B, H, Skv, D),
+                                                                          (B, H, Skv, D)]))
+    tr = (lambda a: np.ascontiguousarray(a.transpose(0, 2, 1, 3))) if seq_major else (lambda a: a)
+    ws, n = ws_fp8(B, H, Sq, Skv, D, out_f32)
+    assert n > 256, "the planner was expected to split this shape"
+    o, lse = cp.attn_fwd_fp8(dev8(tr(q8)), dev8(tr(k8)), dev8(tr(v8)), out_dtype=torch.float32 if out_f32 else None,
+                             seq_major=seq_major, workspace=ws)
+    torch.cuda.synchronize()
+    check_fp8(q8, k8, v8, 1.0, 1.0, 1.0, 1.0 / math.sqrt(D), o.transpose(1, 2) if seq_major else o, lse,
+              "fp8 split", out_f32)
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv", [(1, 24, 4096, 256), (1, 8, 44160, 200)])
+def test_fp8_dynamic_schedule_same_bits(B, H, Sq, Skv):
+    """More tiles than resident workgroups, no split: the counter-claimed units run the same
+    arithmetic as the static order, so the outputs are the same bits (two calls, one workspace)."""
+    log(f"case: fp8 dynamic schedule B{B} H{H} Sq{Sq} Skv{Skv}")
+    q, k, v = (dev8(inputs.random_e4m3((B, H, n, 128), 7500 + i)) for i, n in enumerate((Sq, Skv, Skv)))
+    ws, n = ws_fp8(B, H, Sq, Skv, 128, False)
+    assert n == 256
+    o_ref, l_ref = cp.attn_fwd_fp8(q, k, v)
+    for rep in range(2):
+        o, l = cp.attn_fwd_fp8(q, k, v, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(l, l_ref), rep
+
+
+@pytest.mark.parametrize("use_ws", [False, True], ids=["no_ws", "ws"])
+def test_fp8_accumulate_chunks(use_ws):
+    """A ring step in fp8: chunks of keys folded into an f32 (O, LSE) by the accumulate epilogue
+    (and the piece merge when split) equal attention over all keys within the derived bound;
+    folding into the empty result (O = 0, LSE = -inf) gives the plain call's bits."""
+    H, Sq, D = 2, 600, 128
+    edges = [0, 1000, 1001, 2650]
+    q8 = inputs.random_e4m3((1, H, Sq, D), 7600)
+    k8 = inputs.random_e4m3((1, H, edges[-1], D), 7601)
+    v8 = inputs.random_e4m3((1, H, edges[-1], D), 7602)
+    log(f"case: fp8 accumulate over chunks {edges} use_ws={use_ws}")
+    q = dev8(q8)
+    o = torch.zeros((1, H, Sq, D), dtype=torch.float32, device="cuda")
+    lse = torch.full((1, H, Sq), float("-inf"), device="cuda")
+    for a, b in zip(edges[:-1], edges[1:]):
+        k, v = dev8(np.ascontiguousarray(k8[:, :, a:b])), dev8(np.ascontiguousarray(v8[:, :, a:b]))
+        ws = ws_fp8(1, H, Sq, b - a, D, True)[0] if use_ws else None
+        if a == 0:
+            o_ref, l_ref = cp.attn_fwd_fp8(q, k, v, out_dtype=torch.float32, workspace=ws)
+        cp.attn_fwd_fp8(q, k, v, o=o, lse=lse, workspace=ws, accumulate=True)
+        if a == 0:
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int32), o_ref.view(torch.int32)) and torch.equal(lse, l_ref)
+    torch.cuda.synchronize()
+    check_fp8(q8, k8, v8, 1.0, 1.0, 1.0, 1.0 / math.sqrt(D), o, lse, "fp8 accumulated", out_f32=True)
