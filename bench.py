@@ -508,8 +508,7 @@ def secondary_rows(cp, torch, q, k, v, stream, kt=None, vt=None):
     unpacked = [torch.empty_like(q3) for _ in range(3)]
 
     def unfused():
-        for src, dst in zip(r5, unpacked):
-            cp.ulysses_unpack(src, P, cp.SEQ_TO_HEAD, dst=dst, stream=stream)
+        cp.ulysses_unpack_n(r5, P, cp.SEQ_TO_HEAD, dsts=unpacked, stream=stream)
         cp.attn_fwd_ex(unpacked[0], unpacked[1], unpacked[2], o=o3, lse=l3, workspace=ws3, stream=stream)
         cp.ulysses_pack(o3, P, cp.HEAD_TO_SEQ, dst=o_send.view(1, P, S_L, H // P, D), stream=stream)
 
@@ -670,6 +669,19 @@ def cold_rows(cp, torch, stream, n_sets=12):
     ms = rotate(fns)
     out["unpack_s2h_cold_us"] = round(ms * 1e3, 2)
     out["unpack_s2h_cold_GBps"] = round(nbytes / ms / 1e6, 1)
+    # the same shards as n_sets / 3 batched calls of three (one rank's Q, K, V in one launch)
+    groups = [list(range(i, i + 3)) for i in range(0, n_sets - n_sets % 3, 3)]
+    fns = [lambda g=g: cp.ulysses_pack_n([shards[i] for i in g], P, cp.SEQ_TO_HEAD, dsts=[sends[i] for i in g],
+                                         stream=stream) for g in groups]
+    ms = rotate(fns)
+    out["pack_qkv_s2h_cold_us"] = round(ms * 1e3, 2)
+    out["pack_qkv_s2h_cold_GBps"] = round(3 * nbytes / ms / 1e6, 1)
+    fns = [lambda g=g: cp.ulysses_unpack_n([sends[i] for i in g], P, cp.SEQ_TO_HEAD,
+                                           dsts=[shards[i].view(1, H // P, S_L * P, D) for i in g], stream=stream)
+           for g in groups]
+    ms = rotate(fns)
+    out["unpack_qkv_s2h_cold_us"] = round(ms * 1e3, 2)
+    out["unpack_qkv_s2h_cold_GBps"] = round(3 * nbytes / ms / 1e6, 1)
     return out
 
 

@@ -37,9 +37,10 @@
  *    to the 16-bit type, split score scale) of the attention sample in
  *    "TensorRT multi-device attention inference in practice", step 1.
  *
- *  - ulysses_pack / ulysses_unpack: the sequence<->head relayout on either
- *    side of DeepSpeed Ulysses' two all-to-alls (first page, "DeepSpeed
- *    Ulysses"; 5520 tokens per rank at degree 8 in "Simplifying model
+ *  - ulysses_pack / ulysses_unpack (and the batched _n forms): the
+ *    sequence<->head relayout on either side of DeepSpeed Ulysses' two
+ *    all-to-alls (first page, "DeepSpeed Ulysses"; 5520 tokens per rank at
+ *    degree 8 in "Simplifying model
  *    serving across multiple GPUs with NVIDIA TensorRT multi-device
  *    integration in NVIDIA Dynamo-Triton", section on distributing Cosmos 3
  *    with Ulysses context parallelism).
@@ -79,7 +80,10 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 3
+#define CPATTN_ABI_VERSION 4
+
+/* Bytes of work counters at the head of an attention workspace. */
+#define CPATTN_WORKSPACE_COUNTER_BYTES 2048
 
 typedef enum {
     CPATTN_OK = 0,
@@ -149,18 +153,22 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
  *
  * Workspace.  The bf16 kernel runs 256 query rows of one (b, h) per
  * workgroup, at most one workgroup per resident slot, each looping over
- * units of work.  The first 256 bytes of a workspace hold a work counter:
- * after the first round, units are claimed from it, so the parts of the
- * device that run faster (the XCDs' clocks differ under the power limit)
- * take more of them (the call clears the counter itself, with a kernel).
+ * units of work.  The first CPATTN_WORKSPACE_COUNTER_BYTES bytes of a
+ * workspace hold work counters: after the first round, units are claimed
+ * from them, each XCD from its own contiguous range of units first (its
+ * workgroups then share each head's K and V in its L2), then from a tail
+ * shared by all, so the XCDs that run faster (their clocks differ under the
+ * power limit) take more of it (the call clears the counters itself, with a
+ * kernel).
  * When the tiles do not fill the device's last wave, the keys of the tiles
  * in that wave are also split into pieces that run in parallel, and a
  * second kernel folds the pieces with the attn_merge rule.  The split is
  * planned per call from the device's resident-workgroup count and limited
  * to what the rest of the workspace holds: (D + 1) * 1024 bytes per piece.
- * cpattn_attn_fwd_workspace_size gives the size the best plan uses (256
- * bytes when no split helps); less only means fewer (or no) pieces, and
- * under 256 bytes (or none) also the static unit order of cpattn_attn_fwd.
+ * cpattn_attn_fwd_workspace_size gives the size the best plan uses
+ * (CPATTN_WORKSPACE_COUNTER_BYTES when no split helps); less only means
+ * fewer (or no) pieces, and under CPATTN_WORKSPACE_COUNTER_BYTES (or none)
+ * also the static unit order of cpattn_attn_fwd.
  * f32 inputs never split; bf16 and fp16 inputs share the plan.
  * Results differ from cpattn_attn_fwd's only by f32 rounding in the fold:
  * without a split the two give the same bits.
@@ -306,8 +314,10 @@ cpattn_status cpattn_attn_merge(const void* o_a, const float* lse_a, const void*
  * Chunk 0's attention is written to (o, lse); every later chunk's attention
  * is folded into (o, lse) in its epilogue with the attn_merge rule (f32), as
  * cpattn_attn_fwd_ex with CPATTN_FLAG_ACCUMULATE does.  The work buffers, when
- * given, serve as the workspace (the work counter in the first 256 bytes of
- * lse_work, the key-range pieces in the rest; contents undefined on return).  The result equals attention over the concatenation of all
+ * given, serve as the workspace (the work counters in the first
+ * CPATTN_WORKSPACE_COUNTER_BYTES bytes of lse_work, which must be at least
+ * that long to be used; the key-range pieces in the rest; contents undefined
+ * on return).  The result equals attention over the concatenation of all
  * chunks.  n_chunks >= 1, Skv_chunk >= 0, D in {64, 128}, scale as for
  * attn_fwd.  o, lse, o_work and lse_work must not overlap each other or the
  * inputs.
@@ -328,7 +338,9 @@ cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_chunks, const vo
  *
  * Chunk p of dst is destined for rank p.  A bit-exact copy of elements of
  * type dt.  H % P == 0 (else CPATTN_E_SHAPE); D*sizeof(dt) a multiple of 16
- * bytes; src and dst must not overlap.  Rank r is taken to own tokens
+ * bytes (else CPATTN_E_HEADDIM) and below 2^35 bytes, B*S_local*H at most
+ * 2^32 - 1 rows (else CPATTN_E_SHAPE); src and dst must not overlap.  Rank r
+ * is taken to own tokens
  * [r*S_local, (r+1)*S_local) and heads [r*Hp, (r+1)*Hp).
  */
 cpattn_status cpattn_ulysses_pack(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H,
@@ -349,6 +361,30 @@ cpattn_status cpattn_ulysses_pack(const void* src, void* dst, int64_t B, int64_t
 cpattn_status cpattn_ulysses_unpack(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H,
                                     int64_t D, int64_t P, cpattn_dtype dt, cpattn_dir dir,
                                     hipStream_t stream);
+
+/*
+ * Batched Ulysses relayout: the same relayout as cpattn_ulysses_pack
+ * (cpattn_ulysses_pack_n) or cpattn_ulysses_unpack (cpattn_ulysses_unpack_n)
+ * applied to n_tensors tensors of one shape and type in ONE launch, e.g. the
+ * Q, K and V shards that go into one all-to-all (first page, "DeepSpeed
+ * Ulysses": Q, K and V are exchanged together before attention).  Tensor i is
+ * srcs[i] -> dsts[i]; the result equals n_tensors single calls.
+ *
+ *   srcs, dsts  HOST arrays of n_tensors DEVICE pointers (read during the
+ *               call only; the caller keeps ownership of both arrays)
+ *   n_tensors   1 .. CPATTN_MAX_RELAYOUT_TENSORS (else CPATTN_E_SHAPE)
+ *
+ * Every other requirement is the single call's, for each tensor.  No
+ * destination may overlap any source or another destination
+ * (CPATTN_E_ALIAS); a NULL array or entry is CPATTN_E_NULL.
+ */
+#define CPATTN_MAX_RELAYOUT_TENSORS 8
+cpattn_status cpattn_ulysses_pack_n(const void* const* srcs, void* const* dsts, int64_t n_tensors,
+                                    int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t P,
+                                    cpattn_dtype dt, cpattn_dir dir, hipStream_t stream);
+cpattn_status cpattn_ulysses_unpack_n(const void* const* srcs, void* const* dsts, int64_t n_tensors,
+                                      int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t P,
+                                      cpattn_dtype dt, cpattn_dir dir, hipStream_t stream);
 
 /*
  * QK-RMSNorm prologue of the attention sample ("TensorRT multi-device

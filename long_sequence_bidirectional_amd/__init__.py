@@ -16,6 +16,7 @@ torch provides device memory and streams.
   qk_rmsnorm(x, w, eps=1e-6, post_scale=1.0, out=None)   -> out
   ulysses_pack(src, P, direction, dst=None)               -> dst
   ulysses_unpack(src, P, direction, dst=None)             -> dst
+  ulysses_pack_n / ulysses_unpack_n(srcs, P, direction, dsts=None) -> dsts (one launch)
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ from ._lib import (BF16, E4M3, F16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_T
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_static", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge",
            "qk_rmsnorm", "attn_fwd_fp8", "ring_attn_fwd", "ulysses_pack", "ulysses_unpack",
+           "ulysses_pack_n", "ulysses_unpack_n", "MAX_RELAYOUT_TENSORS",
            "SEQ_TO_HEAD", "HEAD_TO_SEQ", "CpattnError", "lib"]
 
 
@@ -311,3 +313,43 @@ def ulysses_pack(src, P, direction, dst=None, stream=None):
 def ulysses_unpack(src, P, direction, dst=None, stream=None):
     """seq->head: [B,P,S_l,Hp,D] -> [B,Hp,P*S_l,D]; head->seq: [B,P,S_l,Hp,D] -> [B,S_l,P*Hp,D]."""
     return _relayout("cpattn_ulysses_unpack", src, P, direction, dst, False, stream)
+
+
+MAX_RELAYOUT_TENSORS = 8     # CPATTN_MAX_RELAYOUT_TENSORS
+
+
+def _relayout_n(fn, srcs, P, direction, dsts, pack, stream):
+    torch = _torch()
+    srcs = list(srcs)
+    if not 1 <= len(srcs) <= MAX_RELAYOUT_TENSORS:
+        raise ValueError(f"1 to {MAX_RELAYOUT_TENSORS} tensors, got {len(srcs)}")
+    (B, S_l, H, D), out_shape = _relayout_shapes(srcs[0], P, direction, pack)
+    for t in srcs[1:]:
+        if tuple(t.shape) != tuple(srcs[0].shape) or t.dtype != srcs[0].dtype:
+            raise ValueError("every source must have the first one's shape and dtype")
+    if dsts is None:
+        dsts = [torch.empty(out_shape, dtype=srcs[0].dtype, device=srcs[0].device) for _ in srcs]
+    dsts = list(dsts)
+    if len(dsts) != len(srcs):
+        raise ValueError("one destination per source")
+    for t in dsts:
+        if tuple(t.shape) != tuple(out_shape) or t.dtype != srcs[0].dtype:
+            raise ValueError(f"every dst must be {out_shape} of {srcs[0].dtype}")
+    n = len(srcs)
+    src_ptrs = (ctypes.c_void_p * n)(*(_dev(t, f"srcs[{i}]") for i, t in enumerate(srcs)))
+    dst_ptrs = (ctypes.c_void_p * n)(*(_dev(t, f"dsts[{i}]") for i, t in enumerate(dsts)))
+    st = getattr(lib(), fn)(src_ptrs, dst_ptrs, n, B, S_l, H, D, P, _dtype_code(srcs[0]), direction,
+                            _stream(stream))
+    check(fn, st)
+    return dsts
+
+
+def ulysses_pack_n(srcs, P, direction, dsts=None, stream=None):
+    """ulysses_pack of up to 8 same-shaped tensors (e.g. Q, K, V) in one launch; returns the list
+    of destinations."""
+    return _relayout_n("cpattn_ulysses_pack_n", srcs, P, direction, dsts, True, stream)
+
+
+def ulysses_unpack_n(srcs, P, direction, dsts=None, stream=None):
+    """ulysses_unpack of up to 8 same-shaped tensors in one launch; returns the destinations."""
+    return _relayout_n("cpattn_ulysses_unpack_n", srcs, P, direction, dsts, False, stream)

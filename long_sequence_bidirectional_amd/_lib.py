@@ -15,8 +15,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libcpattn.so")
 OK, E_NULL, E_SHAPE, E_DTYPE, E_HEADDIM, E_ALIGN, E_ALIAS, E_HIP, E_SCALE, E_FLAGS = range(10)
 BF16, F32, F16, E4M3 = 0, 1, 2, 3
 SEQ_TO_HEAD, HEAD_TO_SEQ = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 STATIC_SCRATCH_BYTES = 32 << 20     # CPATTN_STATIC_SCRATCH_BYTES
+SCHED_BYTES = 2048                  # CPATTN_WORKSPACE_COUNTER_BYTES
 FLAG_ACCUMULATE = 1
 FLAG_SEQ_MAJOR = 2
 
@@ -28,6 +29,7 @@ STATUS_NAMES = {OK: "OK", E_NULL: "E_NULL", E_SHAPE: "E_SHAPE", E_DTYPE: "E_DTYP
 _P, _I64, _F, _E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
 _U32, _U64 = ctypes.c_uint32, ctypes.c_uint64
 _PI64, _PU64 = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64)
+_PP = ctypes.POINTER(ctypes.c_void_p)
 SIGNATURES = [
     ("cpattn_attn_fwd", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _P]),
     ("cpattn_attn_fwd_ex", _E, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _F, _E, _E, _U32, _P, _U64, _P]),
@@ -41,6 +43,8 @@ SIGNATURES = [
     ("cpattn_qk_rmsnorm", _E, [_P, _P, _P, _I64, _I64, _F, _F, _E, _P]),
     ("cpattn_ulysses_pack", _E, [_P, _P, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),
     ("cpattn_ulysses_unpack", _E, [_P, _P, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),
+    ("cpattn_ulysses_pack_n", _E, [_PP, _PP, _I64, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),
+    ("cpattn_ulysses_unpack_n", _E, [_PP, _PP, _I64, _I64, _I64, _I64, _I64, _I64, _E, _E, _P]),
     ("cpattn_status_string", ctypes.c_char_p, [_E]),
     ("cpattn_abi_version", ctypes.c_int, []),
 ]

@@ -14,6 +14,8 @@
 
 #define CPATTN_EXPORT extern "C" __attribute__((visibility("default")))
 
+static_assert(cpattn::kSchedBytes == CPATTN_WORKSPACE_COUNTER_BYTES, "workspace counter area");
+
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
@@ -173,11 +175,13 @@ cpattn::Strides layout_strides(int64_t H, int64_t S, int64_t D, bool seq_major) 
 
 // Attention of one K/V set into (o, lse): written, or folded into them when accumulate.
 // ws_o/ws_lse (capacity ws_pieces pieces each) hold the partials of a split; null = no split.
-// sched (cpattn::kSchedBytes of device memory) enables the dynamic unit schedule; null = static.
+// sched (a set of cpattn::kSchedSetWords words of device memory) enables the dynamic unit
+// schedule; null = static.  When sched_clear is not null, the cpattn::kSchedWords words there
+// (sched among them) are cleared first; when it is null, sched must already be zero.
 cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                        int64_t Sq, int64_t Skv, int64_t D, float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
                        bool accumulate, bool seq_major, float* ws_o, float* ws_lse, int64_t ws_pieces,
-                       unsigned long long* sched, hipStream_t stream) {
+                       unsigned long long* sched, unsigned long long* sched_clear, hipStream_t stream) {
     const int64_t BH = B * H;
     if (Skv == 0) {   // empty key set: O = 0, LSE = -inf, the identity of the fold
         if (accumulate) return CPATTN_OK;
@@ -205,9 +209,11 @@ cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, flo
     a.split_pieces = 1;
     a.slots = 0;
     a.sched = nullptr;
+    a.sched_clear = nullptr;
     a.stream = stream;
     if (in_dtype == CPATTN_F32) return hip_status(cpattn::launch_attn_fwd_f32(a));
     a.sched = sched;
+    a.sched_clear = sched ? sched_clear : nullptr;
     a.slots = device_slots(D, a.out_f32);
     if (ws_o && ws_lse && ws_pieces > 0) {
         const SplitPlan p = plan_split(BH, Sq, Skv, D, a.slots, (uint64_t)ws_pieces * piece_bytes(D));
@@ -261,7 +267,7 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd(const void* q, const void* k, const 
     const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, &ck);
     if (st != CPATTN_OK) return st;
     return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
-                    static_cast<cpattn_dtype>(odt), false, false, nullptr, nullptr, 0, nullptr, stream);
+                    static_cast<cpattn_dtype>(odt), false, false, nullptr, nullptr, 0, nullptr, nullptr, stream);
 }
 
 namespace {
@@ -297,7 +303,7 @@ cpattn_status run_attn_fwd_ex(const void* q, const void* k, const void* v, void*
     }
     return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
                     static_cast<cpattn_dtype>(odt), (flags & CPATTN_FLAG_ACCUMULATE) != 0,
-                    (flags & CPATTN_FLAG_SEQ_MAJOR) != 0, ws_o, ws_lse, ws_pieces, sched, stream);
+                    (flags & CPATTN_FLAG_SEQ_MAJOR) != 0, ws_o, ws_lse, ws_pieces, sched, sched, stream);
 }
 
 }  // namespace
@@ -434,10 +440,12 @@ CPATTN_EXPORT cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, co
     a.split_pieces = 1;
     a.slots = device_slots(D, a.out_f32, true);
     a.sched = nullptr;
+    a.sched_clear = nullptr;
     a.stream = stream;
     if (workspace && workspace_bytes >= (uint64_t)cpattn::kSchedBytes) {
         // same layout as attn_fwd_ex: counters, then the pieces' O, then their LSE
         a.sched = static_cast<unsigned long long*>(workspace);
+        a.sched_clear = a.sched;
         const int64_t ws_pieces = (int64_t)((workspace_bytes - cpattn::kSchedBytes) / piece_bytes(D));
         const SplitPlan p = plan_split(a.BH, Sq, Skv, D, a.slots, (uint64_t)ws_pieces * piece_bytes(D));
         if (p.split_tiles > 0) {
@@ -554,21 +562,28 @@ CPATTN_EXPORT cpattn_status cpattn_ring_attn_fwd(const void* q, const void* k_ch
     const int64_t ws_pieces =
         work ? std::min(c.rows / cpattn::kAttnTileRows, (c.rows - kSchedFloats) / cpattn::kAttnTileRows) : 0;
     float* ws_lse = work ? lse_work + kSchedFloats : nullptr;
+    // Chunk c takes counter set c % kSchedSets; the launch of every kSchedSets-th chunk clears the
+    // sets of that chunk and the next kSchedSets - 1 (one small kernel per 16 chunks).
     cpattn_status s = CPATTN_OK;
     for (int64_t ch = 0; ch < n_chunks && s == CPATTN_OK; ++ch) {
         const char* kc = static_cast<const char*>(k_chunks) + ch * chunk_bytes;
         const char* vc = static_cast<const char*>(v_chunks) + ch * chunk_bytes;
+        const int64_t w = ch % cpattn::kSchedSets;
         s = run_attn(q, kc, vc, o, lse, B, H, Sq, Skv_chunk, D, scale, CPATTN_BF16, CPATTN_F32, ch > 0, false,
-                     work ? o_work : nullptr, ws_lse, ws_pieces, sched, stream);
+                     work ? o_work : nullptr, ws_lse, ws_pieces, sched ? sched + w * cpattn::kSchedSetWords : nullptr,
+                     (sched && w == 0) ? sched : nullptr, stream);
     }
     return s;
 }
 
 namespace {
 
-cpattn_status relayout(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t P,
-                       int dt, int dir, bool pack, hipStream_t stream) {
-    if (!src || !dst) return CPATTN_E_NULL;
+cpattn_status relayout(const void* const* srcs, void* const* dsts, int64_t n, int64_t B, int64_t S_local, int64_t H,
+                       int64_t D, int64_t P, int dt, int dir, bool pack, hipStream_t stream) {
+    if (!srcs || !dsts) return CPATTN_E_NULL;
+    if (n < 1 || n > cpattn::kMaxRelayoutTensors) return CPATTN_E_SHAPE;
+    for (int64_t i = 0; i < n; ++i)
+        if (!srcs[i] || !dsts[i]) return CPATTN_E_NULL;
     if (!dtype_valid(dt)) return CPATTN_E_DTYPE;
     if (dir != CPATTN_SEQ_TO_HEAD && dir != CPATTN_HEAD_TO_SEQ) return CPATTN_E_SHAPE;
     if (!dims_ok({B, S_local, H, D, P}, 1) || H % P != 0) return CPATTN_E_SHAPE;
@@ -576,12 +591,32 @@ cpattn_status relayout(const void* src, void* dst, int64_t B, int64_t S_local, i
     if (row_bytes % 16 != 0) return CPATTN_E_HEADDIM;
     const int64_t n_rows = prod({B, S_local, H});
     const int64_t bytes = mul_checked(n_rows, row_bytes);
-    // 32-bit row indices in the kernel (its grid strides over the chunks, so their count is free)
-    if (n_rows < 0 || bytes < 0 || n_rows > (int64_t)UINT32_MAX) return CPATTN_E_SHAPE;
-    if (!aligned16(src) || !aligned16(dst)) return CPATTN_E_ALIGN;
-    if (overlap(range(src, bytes), range(dst, bytes))) return CPATTN_E_ALIAS;
+    // 32-bit row indices and 16-byte chunk indices within a row in the kernel (its grid strides
+    // over tiles of rows, so their count is free)
+    if (n_rows < 0 || bytes < 0 || n_rows > (int64_t)UINT32_MAX || row_bytes / 16 > (int64_t)INT32_MAX)
+        return CPATTN_E_SHAPE;
+    for (int64_t i = 0; i < n; ++i)
+        if (!aligned16(srcs[i]) || !aligned16(dsts[i])) return CPATTN_E_ALIGN;
+    // every destination is disjoint from every source and from every other destination
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            if (overlap(range(dsts[i], bytes), range(srcs[j], bytes))) return CPATTN_E_ALIAS;
+            if (j != i && overlap(range(dsts[i], bytes), range(dsts[j], bytes))) return CPATTN_E_ALIAS;
+        }
     const int mode = (dir == CPATTN_SEQ_TO_HEAD ? 0 : 2) + (pack ? 0 : 1);
-    cpattn::RelayoutArgs a{src, dst, B, S_local, H, P, row_bytes, mode, stream};
+    cpattn::RelayoutArgs a{};
+    for (int64_t i = 0; i < n; ++i) {
+        a.ptrs.src[i] = srcs[i];
+        a.ptrs.dst[i] = dsts[i];
+    }
+    a.n_tensors = (int)n;
+    a.B = B;
+    a.S_local = S_local;
+    a.H = H;
+    a.P = P;
+    a.row_bytes = row_bytes;
+    a.mode = mode;
+    a.stream = stream;
     return hip_status(cpattn::launch_relayout(a));
 }
 
@@ -590,13 +625,25 @@ cpattn_status relayout(const void* src, void* dst, int64_t B, int64_t S_local, i
 CPATTN_EXPORT cpattn_status cpattn_ulysses_pack(const void* src, void* dst, int64_t B, int64_t S_local, int64_t H,
                                                 int64_t D, int64_t P, cpattn_dtype dt, cpattn_dir dir,
                                                 hipStream_t stream) {
-    return relayout(src, dst, B, S_local, H, D, P, enum_bits(dt), enum_bits(dir), true, stream);
+    return relayout(&src, &dst, 1, B, S_local, H, D, P, enum_bits(dt), enum_bits(dir), true, stream);
 }
 
 CPATTN_EXPORT cpattn_status cpattn_ulysses_unpack(const void* src, void* dst, int64_t B, int64_t S_local,
                                                   int64_t H, int64_t D, int64_t P, cpattn_dtype dt,
                                                   cpattn_dir dir, hipStream_t stream) {
-    return relayout(src, dst, B, S_local, H, D, P, enum_bits(dt), enum_bits(dir), false, stream);
+    return relayout(&src, &dst, 1, B, S_local, H, D, P, enum_bits(dt), enum_bits(dir), false, stream);
+}
+
+CPATTN_EXPORT cpattn_status cpattn_ulysses_pack_n(const void* const* srcs, void* const* dsts, int64_t n_tensors,
+                                                  int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t P,
+                                                  cpattn_dtype dt, cpattn_dir dir, hipStream_t stream) {
+    return relayout(srcs, dsts, n_tensors, B, S_local, H, D, P, enum_bits(dt), enum_bits(dir), true, stream);
+}
+
+CPATTN_EXPORT cpattn_status cpattn_ulysses_unpack_n(const void* const* srcs, void* const* dsts, int64_t n_tensors,
+                                                    int64_t B, int64_t S_local, int64_t H, int64_t D, int64_t P,
+                                                    cpattn_dtype dt, cpattn_dir dir, hipStream_t stream) {
+    return relayout(srcs, dsts, n_tensors, B, S_local, H, D, P, enum_bits(dt), enum_bits(dir), false, stream);
 }
 
 namespace {

@@ -43,6 +43,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "unit_sched.h"
 
 #define CPATTN_AI __attribute__((always_inline))
 
@@ -396,6 +397,11 @@ __device__ __forceinline__ int attn_unit_fp8(int k_unit, const uint8_t* __restri
         body(ic<3>{}, T{}, T{}, j + 2, T{});
         body(ic<0>{}, T{}, T{}, j + 3, T{});
     }
+    // Dynamic schedule: claim the next unit now, a few blocks before the end, so that the
+    // atomic's round trip overlaps the last blocks (it is complete by the end of the next
+    // softmax slot, and its result is first read after the epilogue).
+    unsigned long long claim = 0;
+    if (map.sched != nullptr && tid == 0) claim = sched_ticket(map, k_unit, (int)blockIdx.x);
     for (; j + 3 < nblk; j += 4) {
         body(ic<1>{}, T{}, T{}, j);
         body(ic<2>{}, T{}, T{}, j + 1);
@@ -412,9 +418,6 @@ __device__ __forceinline__ int attn_unit_fp8(int k_unit, const uint8_t* __restri
         default: body(ic<3>{}, F{}, T{}, nblk); break;
     }
     if (group == 0) slot_barrier();
-    unsigned long long claim = 0;
-    if (map.sched != nullptr && tid == 0)
-        claim = __hip_atomic_fetch_add(map.sched, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // epilogue: l carries the 2^7 of the weights; O = acc * v_scale / l, LSE natural
     const float l_tot = sum_across_halves(l_run);
@@ -479,9 +482,9 @@ __device__ __forceinline__ int attn_unit_fp8(int k_unit, const uint8_t* __restri
     // the claim is first used here, after the epilogue's stores are issued; every wave read the
     // previous one before the first barrier of this unit
     __builtin_amdgcn_sched_barrier(0);
-    if (tid == 0) *next_lds = (int)min(claim, (unsigned long long)INT_MAX - (unsigned long long)gridDim.x);
+    if (tid == 0) *next_lds = sched_next(map, k_unit, (int)blockIdx.x, (int)gridDim.x, claim);
     __syncthreads();
-    return *next_lds + (int)gridDim.x;
+    return *next_lds;
 }
 
 // Persistent workgroups over work units, with the static or the dynamic schedule of the 16-bit
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     int64_t bid = bb;
     int u;
     if (dynamic) {
-        u = n_units >= G ? (bb % kNumXcd) * (G / kNumXcd) + bb / kNumXcd : bb;
+        u = sched_first(map, bb);
     } else {
         u = -1;
         for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
@@ -526,8 +529,10 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     }
 }
 
+
+// Clears the dynamic schedule's counters (kSchedWords words) before a launch that uses one.
 __global__ void zero_sched_kernel_fp8(unsigned long long* sched) {
-    if (threadIdx.x < kSchedWords) sched[threadIdx.x] = 0;
+    for (int i = threadIdx.x; i < kSchedWords; i += blockDim.x) sched[i] = 0;
 }
 
 template <bool OUT_F32, bool SEQ>
@@ -549,8 +554,9 @@ hipError_t launch_fp8_typed(const AttnFp8Args& a) {
     const float c = (float)((double)a.scale * 1.4426950408889634 * (double)a.q_scale * (double)a.k_scale);
     const int64_t cap = a.slots - a.slots % kNumXcd;
     const int launch_grid = (cap > 0 && grid > cap) ? (int)cap : grid;
-    if (m.sched != nullptr) {
-        hipLaunchKernelGGL(zero_sched_kernel_fp8, dim3(1), dim3(64), 0, a.stream, m.sched);
+    m.per_xcd = a.sched != nullptr ? sched_per_xcd(m.n_dp, launch_grid) : 0;
+    if (a.sched != nullptr && a.sched_clear) {
+        hipLaunchKernelGGL(zero_sched_kernel_fp8, dim3(1), dim3(256), 0, a.stream, a.sched_clear);
         const hipError_t ez = hipGetLastError();
         if (ez != hipSuccess) return ez;
     }

@@ -83,6 +83,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "unit_sched.h"
 
 #ifndef CPATTN_AI
 #define CPATTN_AI __attribute__((always_inline))
@@ -141,13 +142,15 @@ __device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
 // and its LSE in workspace slot ti * s + p.
 //
 // With a dynamic schedule (map.sched) the lane that claims work takes the next unit from the
-// counter right after the block loop, so the atomic's latency overlaps the epilogue; the claim
-// is passed to every wave through *next_lds and returned (-1 without a dynamic schedule).
+// counter a few blocks before the end of this one, so the atomic's latency overlaps the last
+// blocks; the claim is passed to every wave through *next_lds after the epilogue and returned
+// (-1 without a dynamic schedule).
 template <int D, bool F16, bool OUT_F32, bool SEQ>
 __device__ __forceinline__ int attn_unit(
-    int k_unit, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
-    Strides so, AttnTileMap map, float c, int* next_lds) {
+    int k_unit, bool first, int static_next, u32x4 (&qreg)[D / 16], const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
+    int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv, Strides so, AttnTileMap map, float c,
+    int* next_lds) {
     constexpr int BN = kBN;
     constexpr int NC = D / 8;               // 16-byte chunks per row
     constexpr int NKS = D / 16;             // k-steps of the QK^T product
@@ -164,23 +167,6 @@ __device__ __forceinline__ int attn_unit(
     __shared__ __attribute__((aligned(1024))) uint16_t Ks[NBUF][BN * D];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs[NBUF][BN * D];
 
-    const int nblk_all = (Skv_all + BN - 1) / BN;
-    int tile, kb0 = 0, slot = -1, nblk = nblk_all;
-    if (k_unit < map.n_dp) {
-        tile = k_unit;
-    } else {
-        const int logical = k_unit - map.n_dp;
-        const int p = logical / map.n_split;
-        const int ti = logical - p * map.n_split;
-        tile = map.n_dp + ti;
-        slot = ti * map.split_s + p;
-        kb0 = (int)((int64_t)p * nblk_all / map.split_s);
-        nblk = (int)((int64_t)(p + 1) * nblk_all / map.split_s) - kb0;
-    }
-    const int Skv = min(Skv_all - kb0 * BN, nblk * BN);   // keys of this unit
-    const int bh = tile / nQt;
-    const int qt = tile - bh * nQt;
-
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -193,14 +179,53 @@ __device__ __forceinline__ int attn_unit(
 
     // Row strides: D for head-major operands (compile time), runtime for sequence-major ones.
     const int64_t q_row = SEQ ? sq.row : D, kv_row = SEQ ? skv.row : D, o_row = SEQ ? so.row : D;
-    const int b = SEQ ? bh / H : 0, h = SEQ ? bh - b * H : 0;
-    const int64_t q_base = SEQ ? b * sq.batch + h * sq.head : (int64_t)bh * Sq * D;
-    const int64_t o_base = SEQ ? b * so.batch + h * so.head : (int64_t)bh * Sq * D;
-    const int64_t kv_off = (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv_all * D) + (int64_t)kb0 * BN * kv_row;
-    const uint16_t* qp = q + q_base;
-    const uint16_t* kp = k + kv_off;
-    const uint16_t* vp = v + kv_off;
-    const int qrow = qt * kBM + wave * 32 + l32;
+
+    // Where a work unit's data lives: its query tile, key range and output rows.
+    struct Geom {
+        const uint16_t* qp;
+        const uint16_t* kp;
+        const uint16_t* vp;
+        int64_t o_base;
+        int bh, qrow, row0, Skv, nblk, slot;      // row0: the tile's first query row
+    };
+    auto geom = [&](int ku) CPATTN_AI -> Geom {
+        const int nblk_all = (Skv_all + BN - 1) / BN;
+        int tile, kb0 = 0, slot = -1, nb = nblk_all;
+        if (ku < map.n_dp) {
+            tile = ku;
+        } else {
+            const int logical = ku - map.n_dp;
+            const int p = logical / map.n_split;
+            const int ti = logical - p * map.n_split;
+            tile = map.n_dp + ti;
+            slot = ti * map.split_s + p;
+            kb0 = (int)((int64_t)p * nblk_all / map.split_s);
+            nb = (int)((int64_t)(p + 1) * nblk_all / map.split_s) - kb0;
+        }
+        const int bh = tile / nQt;
+        const int qt = tile - bh * nQt;
+        const int b = SEQ ? bh / H : 0, h = SEQ ? bh - b * H : 0;
+        const int64_t q_base = SEQ ? b * sq.batch + h * sq.head : (int64_t)bh * Sq * D;
+        const int64_t kv_off =
+            (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv_all * D) + (int64_t)kb0 * BN * kv_row;
+        Geom g;
+        g.qp = q + q_base;
+        g.kp = k + kv_off;
+        g.vp = v + kv_off;
+        g.o_base = SEQ ? b * so.batch + h * so.head : (int64_t)bh * Sq * D;
+        g.bh = bh;
+        g.qrow = qt * kBM + wave * 32 + l32;
+        g.row0 = qt * kBM;
+        g.Skv = min(Skv_all - kb0 * BN, nb * BN);   // keys of the unit
+        g.nblk = nb;
+        g.slot = slot;
+        return g;
+    };
+    const Geom cur = geom(k_unit);
+    const int Skv = cur.Skv, nblk = cur.nblk, slot = cur.slot, bh = cur.bh, qrow = cur.qrow;
+    const int64_t o_base = cur.o_base;
+    const uint16_t* kp = cur.kp;
+    const uint16_t* vp = cur.vp;
 
     // ---- direct global -> LDS loads of K/V blocks.  Each wave moves its LOADS_PER_WAVE 1 KB
     // pieces of a block; the per-lane byte offsets within a full block are constant, so a load
@@ -224,34 +249,51 @@ __device__ __forceinline__ int attn_unit(
                      :: "v"(off), "s"(sb), "s"(lds), "n"(I * 1024) : "memory", "m0");
 #pragma clang diagnostic pop
     };
-    auto load_piece = [&]<int I>(ic<I>, const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
+    // (skv: the unit's key count; the last, partial block clamps its rows to the last key)
+    auto load_piece = [&]<int I>(ic<I>, const uint16_t* src, uint16_t* dst, int j, bool is_v, int skv_u) CPATTN_AI {
         const uint32_t lds = (uint32_t)(uintptr_t)LDS_PTR(void, dst + wave_u * LOADS_PER_WAVE * 512);
         const char* blk = reinterpret_cast<const char*>(src + (int64_t)j * BN * kv_row);
-        if ((j + 1) * BN <= Skv) {
+        if ((j + 1) * BN <= skv_u) {
             if (is_v) dma(ic<I>{}, voffb[I], blk, lds);
             else dma(ic<I>{}, koffb[I], blk, lds);
         } else {
             const int row = (wave_u * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
             const int ch = (lane % NC) ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
-            const int r = min(row, Skv - 1 - j * BN);
+            const int r = min(row, skv_u - 1 - j * BN);
             dma(ic<I>{}, (uint32_t)((r * kv_row + ch * 8) * 2), blk, lds);
         }
     };
-    auto load_block = [&](const uint16_t* src, uint16_t* dst, int j, bool is_v) CPATTN_AI {
-        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI { (load_piece(ic<Is>{}, src, dst, j, is_v), ...); }(
-            std::make_integer_sequence<int, LOADS_PER_WAVE>{});
+    auto load_block = [&](const uint16_t* src, uint16_t* dst, int j, bool is_v, int skv_u) CPATTN_AI {
+        [&]<int... Is>(std::integer_sequence<int, Is...>) CPATTN_AI {
+            (load_piece(ic<Is>{}, src, dst, j, is_v, skv_u), ...);
+        }(std::make_integer_sequence<int, LOADS_PER_WAVE>{});
     };
-    auto wait_loads = [&]() CPATTN_AI { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-    // Q^T operand of this wave, held in registers for the whole tile: for k-step ks lane
-    // (l32, hh) holds q[row l32][16 ks + 8 hh .. +7], read straight from global memory
-    // (rows past Sq clamped to the last valid one).
-    u32x4 qreg[NKS];
-    {
-        const uint16_t* qr = qp + min(qrow, Sq - 1) * q_row + 8 * hh;
+    // A unit's prologue: its first K/V blocks (K_0..K_2, V_0, V_1) into the LDS buffers of their
+    // index, then its Q^T operand into qreg (held for the whole unit: for k-step ks lane (l32, hh)
+    // holds q[row l32][16 ks + 8 hh .. +7], rows past Sq clamped to the last valid one).  Issued
+    // for the first unit here and for every later unit at the end of the unit before it, once no
+    // wave reads the LDS buffers any more, so its latency overlaps that unit's epilogue.
+    auto issue_prologue = [&](const Geom& g) CPATTN_AI {
+        load_block(g.kp, Ks[0], 0, false, g.Skv);
+        if (g.nblk > 1) load_block(g.kp, Ks[1], 1, false, g.Skv);
+        if (g.nblk > 2) load_block(g.kp, Ks[2], 2, false, g.Skv);
+        load_block(g.vp, Vs[0], 0, true, g.Skv);
+        if (g.nblk > 1) load_block(g.vp, Vs[1], 1, true, g.Skv);
+        const uint16_t* qr = g.qp + min(g.qrow, Sq - 1) * q_row + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qreg[ks] = *reinterpret_cast<const u32x4*>(qr + 16 * ks);
-    }
+    };
+    // Wait for the prologue.  Vector memory operations complete in issue order and the Q loads
+    // are its last ones, so the compiler's wait for qreg (before these empty statements that read
+    // it) covers the K/V loads too, yet not the epilogue stores issued after them: the compiler
+    // counts those stores and leaves them in flight.  The statements also redefine qreg, so no
+    // later use of it waits again (such a wait would also wait for the stores, and for any K/V
+    // loads issued since).
+    auto wait_prologue = [&]() CPATTN_AI {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qreg[ks]));
+    };
 
     // ---- LDS read addresses: lane-dependent parts (elements); the rest folds into offsets
     int koff[NKS], voff[NDT];
@@ -351,7 +393,7 @@ __device__ __forceinline__ int attn_unit(
                 dma(ic<P>{}, koffb[P], reinterpret_cast<const char*>(kp + (int64_t)(j + 3) * BN * kv_row),
                     (uint32_t)(uintptr_t)LDS_PTR(void, Ks[(R + 3) % 4] + wave_u * LOADS_PER_WAVE * 512));
             } else {
-                if (j + 3 < nblk) load_piece(ic<P>{}, kp, Ks[(R + 3) % 4], j + 3, false);
+                if (j + 3 < nblk) load_piece(ic<P>{}, kp, Ks[(R + 3) % 4], j + 3, false, Skv);
             }
         } else {
             constexpr int Q = P - LOADS_PER_WAVE;
@@ -359,7 +401,7 @@ __device__ __forceinline__ int attn_unit(
                 dma(ic<Q>{}, voffb[Q], reinterpret_cast<const char*>(vp + (int64_t)(j + 2) * BN * kv_row),
                     (uint32_t)(uintptr_t)LDS_PTR(void, Vs[(R + 2) % 4] + wave_u * LOADS_PER_WAVE * 512));
             } else {
-                if (j + 2 < nblk) load_piece(ic<Q>{}, vp, Vs[(R + 2) % 4], j + 2, true);
+                if (j + 2 < nblk) load_piece(ic<Q>{}, vp, Vs[(R + 2) % 4], j + 2, true, Skv);
             }
         }
     };
@@ -444,13 +486,11 @@ __device__ __forceinline__ int attn_unit(
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
-    load_block(kp, Ks[0], 0, false);
-    if (nblk > 1) load_block(kp, Ks[1], 1, false);
-    if (nblk > 2) load_block(kp, Ks[2], 2, false);
-    load_block(vp, Vs[0], 0, true);
-    if (nblk > 1) load_block(vp, Vs[1], 1, true);
-    wait_loads();
-    __syncthreads();
+    if (first) {
+        issue_prologue(cur);
+        wait_prologue();
+    }
+    __syncthreads();      // every wave has waited for its own prologue loads
 
     // Both groups run M_0, SM_0, M_1, SM_1, ..., M_nblk; group 1 starts one slot late (an
     // extra barrier up front; group 0 adds one at the end), so on every SIMD one wave is in
@@ -495,6 +535,11 @@ __device__ __forceinline__ int attn_unit(
         body(ic<3>{}, T{}, T{}, T{}, j + 2, T{});
         body(ic<0>{}, T{}, T{}, T{}, j + 3, T{});
     }
+    // Dynamic schedule: claim the next unit now, a few blocks before the end, so that the
+    // atomic's round trip overlaps the last blocks (it is complete by the end of the next
+    // softmax slot, and its result is first read after the epilogue).
+    unsigned long long claim = 0;
+    if (map.sched != nullptr && tid == 0) claim = sched_ticket(map, k_unit, (int)blockIdx.x);
     for (; j + 3 < nblk; j += 4) {
         body(ic<1>{}, T{}, T{}, T{}, j);
         body(ic<2>{}, T{}, T{}, T{}, j + 1);
@@ -504,6 +549,11 @@ __device__ __forceinline__ int attn_unit(
     if (j < nblk) body(ic<1>{}, T{}, T{}, T{}, j);
     if (j + 1 < nblk) body(ic<2>{}, T{}, T{}, T{}, j + 1);
     if (j + 2 < nblk) body(ic<3>{}, T{}, T{}, T{}, j + 2);
+    // The claimed unit goes to every wave through LDS; the barriers of the last body order it.
+    if (map.sched != nullptr && tid == 0) {
+        *next_lds = sched_next(map, k_unit, (int)blockIdx.x, (int)gridDim.x, claim);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
     switch (nblk & 3) {      // M_nblk: the last PV product only
         case 0: body(ic<0>{}, F{}, T{}, F{}, nblk); break;
         case 1: body(ic<1>{}, F{}, T{}, F{}, nblk); break;
@@ -511,16 +561,52 @@ __device__ __forceinline__ int attn_unit(
         default: body(ic<3>{}, F{}, T{}, F{}, nblk); break;
     }
     if (group == 0) slot_barrier();
-    unsigned long long claim = 0;
-    if (map.sched != nullptr && tid == 0)
-        claim = __hip_atomic_fetch_add(map.sched, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // No wave reads LDS from here on: the next unit's prologue goes out now, ahead of this unit's
+    // epilogue (an accumulating epilogue first issues its own loads of the old O, so that its
+    // wait does not also cover the prologue's).
+    const int n_units = map.n_dp + map.n_split * map.split_s;
+    // (read from LDS by every lane; readfirstlane tells the compiler the unit is wave-uniform, so
+    // the branches on it below are scalar ones)
+    const int next = map.sched != nullptr ? __builtin_amdgcn_readfirstlane(*next_lds) : static_next;
+    const bool has_next = next >= 0 && next < n_units;
 
     // ---- epilogue: O = O / l, LSE = (m + log2 l) ln 2; a piece goes to the workspace, an
     // accumulating call folds the result into the (O, LSE) already in o/lse.
+    // Accumulating rows load every old value they fold in first (the stores below go to the same
+    // rows, so loads written after them could not move ahead of them and would each wait out a
+    // round trip), then the next unit's prologue goes out (wave-uniform), then the arithmetic.
+    // A lane whose row is past Sq works on row Sq - 1 (its Q, old O and LSE are that row's), so it
+    // stores that row's own bits again: every wave issues the same stores on every path, which
+    // lets the compiler's wait for the next prologue leave them all in flight.
+    const bool acc_rows = OUT_F32 && map.accumulate && slot < 0;
+    const int srow = min(qrow, Sq - 1);
+    f32x4 old[OUT_F32 ? NDT * 4 : 1];
+    float la = -INFINITY;
+    if constexpr (OUT_F32) {
+        if (acc_rows) {
+            const int64_t orow = o_base + srow * o_row;
+            la = lse[(size_t)bh * Sq + srow];
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    old[dt * 4 + g] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow +
+                                                                      dt * 32 + g * 8 + hh * 4);
+            // In the tile that holds row Sq - 1, lanes of other waves also read that row (their rows
+            // are past Sq) and write it back: every wave has its old values before any wave stores.
+            if (cur.row0 + kBM > Sq) {
+                asm volatile("" : "+v"(la));
+#pragma unroll
+                for (int i = 0; i < NDT * 4; ++i) asm volatile("" : "+v"(old[i]));
+                __syncthreads();
+            }
+        }
+    }
+    if (has_next) issue_prologue(geom(next));
     const float l_tot = sum_across_halves(l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     const float lse_new = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-    if (slot >= 0) {
+    if (__builtin_amdgcn_readfirstlane(slot) >= 0) {      // wave-uniform: a scalar branch
         const size_t wrow = (size_t)slot * kBM + wave * 32 + l32;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -531,60 +617,66 @@ __device__ __forceinline__ int attn_unit(
                     f32x4{oacc[dt][g * 4 + 0] * inv, oacc[dt][g * 4 + 1] * inv, oacc[dt][g * 4 + 2] * inv,
                           oacc[dt][g * 4 + 3] * inv};
             }
-        if (hh == 0) map.ws_lse[wrow] = lse_new;
-    } else if (qrow < Sq) {
-        const int64_t orow = o_base + qrow * o_row;
+        map.ws_lse[wrow] = lse_new;                // both lane halves hold the same value
+        // The wait for the next prologue sits in each branch, in straight-line code after the Q
+        // loads, so the compiler counts the stores between them; it is unconditional, so no path
+        // back to the loop leaves qreg pending (without a next unit it returns at once).
+        wait_prologue();
+    } else {
+        const int64_t orow = o_base + srow * o_row;
         float wa = 0.f, wb = inv, L = lse_new;   // O = wa * O_old + wb * acc
-        // Accumulating: every old value this lane folds in is loaded before any store (the stores
-        // go to the same rows, so loads written after them could not be moved ahead of them and
-        // would each wait out a full round trip).
-        f32x4 old[OUT_F32 ? NDT * 4 : 1];
-        if constexpr (OUT_F32) {
-            if (map.accumulate) {
-                const float la = lse[(size_t)bh * Sq + qrow];
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        old[dt * 4 + g] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow +
-                                                                          dt * 32 + g * 8 + hh * 4);
-                const float mx = fmaxf(la, lse_new);
-                wb = 0.f;
-                L = -INFINITY;
-                if (mx != -INFINITY) {
-                    const float ea = expf(la - mx), eb = expf(lse_new - mx);
-                    const float tot = ea + eb;
-                    L = mx + logf(tot);
-                    wa = ea / tot;
-                    wb = eb / tot * inv;
-                }
+        if (acc_rows) {
+            const float mx = fmaxf(la, lse_new);
+            wb = 0.f;
+            L = -INFINITY;
+            if (mx != -INFINITY) {
+                const float ea = expf(la - mx), eb = expf(lse_new - mx);
+                const float tot = ea + eb;
+                L = mx + logf(tot);
+                wa = ea / tot;
+                wb = eb / tot * inv;
             }
         }
+        if constexpr (OUT_F32) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = dt * 32 + g * 8 + hh * 4;
-                f32x4 x = f32x4{oacc[dt][g * 4 + 0], oacc[dt][g * 4 + 1], oacc[dt][g * 4 + 2],
-                                oacc[dt][g * 4 + 3]} * wb;
-                if constexpr (OUT_F32) {
-                    if (map.accumulate) x += old[dt * 4 + g] * wa;
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = dt * 32 + g * 8 + hh * 4;
+                    f32x4 x = f32x4{oacc[dt][g * 4 + 0], oacc[dt][g * 4 + 1], oacc[dt][g * 4 + 2],
+                                    oacc[dt][g * 4 + 3]} * wb;
+                    if (acc_rows) x += old[dt * 4 + g] * wa;
                     *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + d0) = x;
-                } else {
-                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + d0) =
-                        u32x2{pack16x2<F16>(x[0], x[1]), pack16x2<F16>(x[2], x[3])};
                 }
-            }
-        if (hh == 0) lse[(size_t)bh * Sq + qrow] = L;
+        } else {
+            // Lane half hh holds columns 8g + 4hh .. +3 of each 8-column group g.  For each pair of
+            // groups (2p, 2p + 1) the halves swap one packed pair (v_permlane32_swap) so that half
+            // hh holds all 8 columns of group 2p + hh and stores them as one 16-byte piece.
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    u32x2 pk[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int g = 2 * p + e;
+                        const f32x4 x = f32x4{oacc[dt][g * 4 + 0], oacc[dt][g * 4 + 1], oacc[dt][g * 4 + 2],
+                                              oacc[dt][g * 4 + 3]} * wb;
+                        pk[e] = u32x2{pack16x2<F16>(x[0], x[1]), pack16x2<F16>(x[2], x[3])};
+                    }
+                    // low half: {own group 2p, the high half's group 2p}; high half: {the low half's
+                    // group 2p + 1, own group 2p + 1}
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+                    const int d0 = dt * 32 + (2 * p + hh) * 8;
+                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(o) + orow + d0) =
+                        u32x4{(uint32_t)s0[0], (uint32_t)s1[0], (uint32_t)s0[1], (uint32_t)s1[1]};
+                }
+        }
+        lse[(size_t)bh * Sq + srow] = L;           // both lane halves hold the same value
+        wait_prologue();
     }
-    if (map.sched == nullptr) return -1;
-    // Every wave read the previous claim before the first barrier of this unit, so the slot
-    // is free; after this barrier every wave sees the new one.  (The claim is first used here,
-    // after the epilogue's stores are issued.)
-    __builtin_amdgcn_sched_barrier(0);
-    if (tid == 0) *next_lds = (int)min(claim, (unsigned long long)INT_MAX - (unsigned long long)gridDim.x);
-    __syncthreads();
-    return *next_lds + (int)gridDim.x;
+    return has_next ? next : -1;
 }
 
 // At most one workgroup per resident slot (gridDim.x of them, a multiple of the XCD count), each
@@ -597,11 +689,7 @@ __device__ __forceinline__ int attn_unit(
 // whole tiles (then of pieces): the workgroups resident on one XCD share a head's K/V stream in
 // its L2.
 //
-// Dynamic schedule (map.sched, zeroed before the launch): the first round is the same XCD-aware
-// map over the first gridDim.x units; every later unit is claimed from the counter in unit order,
-// so XCDs that run faster (their clocks differ under the power limit) take more units, and the
-// workgroups of one XCD, which finish their units together, claim neighbouring tiles together.
-// Every claim advances the counter, so each unit runs once and every workgroup leaves the loop.
+// Dynamic schedule (map.sched): per-XCD ranges of units with a shared tail (unit_sched.h).
 template <int D, bool F16, bool OUT_F32, bool SEQ>
 __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -623,27 +711,25 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     const int G = (int)gridDim.x;
     const int b = (int)blockIdx.x;
     int64_t bid = b;                       // static schedule: next grid id (64-bit: no overflow near INT_MAX)
-    int u;
-    if (dynamic) {
-        u = n_units >= G ? (b % kNumXcd) * (G / kNumXcd) + b / kNumXcd : b;
-    } else {
-        u = -1;
+    auto next_static = [&]() -> int {
+        int u = -1;
         for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
-    }
+        return u;
+    };
+    int u = dynamic ? sched_first(map, b) : next_static();
+    u32x4 qreg[D / 16];                    // the current unit's Q^T operand (loaded by its prologue)
+    bool first = true;
     while (u >= 0 && u < n_units) {       // one call site: the unit body is inlined once
-        const int claimed =
-            attn_unit<D, F16, OUT_F32, SEQ>(u, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv, so, map, c, &next_unit);
-        if (dynamic) {
-            u = claimed;
-        } else {
-            u = -1;
-            for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
-        }
+        const int after = dynamic ? -1 : next_static();
+        u = attn_unit<D, F16, OUT_F32, SEQ>(u, first, after, qreg, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv,
+                                            so, map, c, &next_unit);
+        first = false;
     }
 }
 
+// Clears the dynamic schedule's counters (kSchedWords words) before a launch that uses one.
 __global__ void zero_sched_kernel(unsigned long long* sched) {
-    if (threadIdx.x < kSchedWords) sched[threadIdx.x] = 0;
+    for (int i = threadIdx.x; i < kSchedWords; i += blockDim.x) sched[i] = 0;
 }
 
 template <int D, bool F16, bool OUT_F32, bool SEQ>
@@ -665,8 +751,9 @@ hipError_t launch(const AttnFwdArgs& a) {
     const float c = (float)((double)a.scale * 1.4426950408889634);
     const int64_t cap = a.slots - a.slots % kNumXcd;
     const int launch_grid = (cap > 0 && grid > cap) ? (int)cap : grid;
-    if (m.sched != nullptr) {
-        hipLaunchKernelGGL(zero_sched_kernel, dim3(1), dim3(64), 0, a.stream, m.sched);
+    m.per_xcd = a.sched != nullptr ? sched_per_xcd(m.n_dp, launch_grid) : 0;
+    if (a.sched != nullptr && a.sched_clear) {
+        hipLaunchKernelGGL(zero_sched_kernel, dim3(1), dim3(256), 0, a.stream, a.sched_clear);
         const hipError_t ez = hipGetLastError();
         if (ez != hipSuccess) return ez;
     }

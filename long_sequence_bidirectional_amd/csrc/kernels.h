@@ -44,14 +44,22 @@ struct AttnFwdArgs {
     // Workgroups of the 16-bit kernel resident at once on the current device (0 = unknown):
     // the kernel is launched with at most that many workgroups, each looping over work units.
     int64_t slots;
-    // Work counter of the dynamic unit schedule (kSchedWords words of device memory, zeroed by
-    // the launcher before the kernel runs), or null for the static schedule.
+    // Counter set of the dynamic unit schedule (kSchedSetWords words of device memory that are
+    // zero when the kernel starts), or null for the static schedule.  sched_clear, when not null,
+    // is the first of kSchedWords words (sched among them) that the launcher clears with a small
+    // kernel before the attention kernel; null when the caller cleared sched already (the ring
+    // driver clears the sets of up to kSchedSets chunks with one launch).
     unsigned long long* sched;
+    unsigned long long* sched_clear;
     hipStream_t stream;
 };
 
-// Words (and bytes) of the dynamic schedule's counter area at the start of a workspace.
-constexpr int kSchedWords = 32;
+// The dynamic schedule's counters: one set of kSchedSetWords words per launch (word x < 8 serves
+// XCD x's own range of units, word 8 the shared tail), kSchedSets sets at the start of a
+// workspace (a ring of launches takes one set each before they are cleared again).
+constexpr int kSchedSetWords = 16;
+constexpr int kSchedSets = 16;
+constexpr int kSchedWords = kSchedSetWords * kSchedSets;
 constexpr int kSchedBytes = kSchedWords * 8;
 
 // Kernel-side form of the work split (passed by value).
@@ -61,8 +69,22 @@ struct AttnTileMap {
     float* ws_o;
     float* ws_lse;
     int accumulate;
-    unsigned long long* sched;          // dynamic schedule's counter, or null
+    unsigned long long* sched;          // dynamic schedule's counter set, or null
+    int per_xcd;                        // units [x*per_xcd, (x+1)*per_xcd) form XCD x's range
 };
+
+// Size of each XCD's own range of units under the dynamic schedule, for n_dp whole tiles and a
+// grid of G workgroups (a multiple of the XCD count).  The ranges hold whole rounds of whole
+// tiles (G per round), as many as fit in 7/8 of them and at least one; the rest of the whole
+// tiles and every split piece (a fraction of a tile's work) form the tail shared by all XCDs, so
+// the ranges carry equal work.  0 (no ranges, every unit from the shared counter) when the whole
+// tiles do not fill one round.
+inline int sched_per_xcd(int64_t n_dp, int64_t G) {
+    const int64_t gx = G / 8;
+    if (gx <= 0 || n_dp < G) return 0;
+    const int64_t rounds = n_dp * 7 / (8 * G);
+    return (int)(gx * (rounds > 1 ? rounds : 1));
+}
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f16(const AttnFwdArgs& a);
@@ -88,6 +110,7 @@ struct AttnFp8Args {
     float* ws_lse;
     int64_t slots;
     unsigned long long* sched;
+    unsigned long long* sched_clear;
     hipStream_t stream;
 };
 
@@ -166,9 +189,14 @@ hipError_t launch_qk_rmsnorm(const QkNormArgs& a);
 
 // Relayout modes (see cpattn.h): 0 pack seq->head, 1 unpack seq->head,
 // 2 pack head->seq, 3 unpack head->seq.
+constexpr int kMaxRelayoutTensors = 8;
+struct RelayoutPtrs {                 // passed to the kernel by value
+    const void* src[kMaxRelayoutTensors];
+    void* dst[kMaxRelayoutTensors];
+};
 struct RelayoutArgs {
-    const void* src;
-    void* dst;
+    RelayoutPtrs ptrs;   // the first n_tensors entries are used
+    int n_tensors;       // 1 .. kMaxRelayoutTensors, all of the same shape
     int64_t B, S_local, H, P;
     int64_t row_bytes;   // D * element size, a multiple of 16
     int mode;

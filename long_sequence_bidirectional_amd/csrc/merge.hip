@@ -156,19 +156,48 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restri
     const int64_t orow = (bh / H) * so.batch + (bh % H) * so.head + qrow * so.row;   // o offset
     const float* lp = ws_lse + (size_t)ti * pieces * TR + r;
     const float* op = ws_o + ((size_t)ti * pieces * TR + r) * D + c4;
+    // The pieces' values are read in batches of independent loads (indices clamped to the last
+    // piece, values past it ignored), so each batch costs one memory round trip rather than one
+    // per piece.
+    constexpr int LB = 16, OB = 8;
     const float la = accumulate ? lse[row] : -INFINITY;
     float mx = la;
-    for (int p = 0; p < pieces; ++p) mx = fmaxf(mx, lp[(size_t)p * TR]);
+    for (int p0 = 0; p0 < pieces; p0 += LB) {
+        float l[LB];
+#pragma unroll
+        for (int i = 0; i < LB; ++i) l[i] = lp[(size_t)min(p0 + i, pieces - 1) * TR];
+#pragma unroll
+        for (int i = 0; i < LB; ++i)
+            if (p0 + i < pieces) mx = fmaxf(mx, l[i]);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = -INFINITY;
     if (mx != -INFINITY) {
         float tot = expf(la - mx);
-        for (int p = 0; p < pieces; ++p) tot += expf(lp[(size_t)p * TR] - mx);
+        for (int p0 = 0; p0 < pieces; p0 += LB) {
+            float l[LB];
+#pragma unroll
+            for (int i = 0; i < LB; ++i) l[i] = lp[(size_t)min(p0 + i, pieces - 1) * TR];
+#pragma unroll
+            for (int i = 0; i < LB; ++i)
+                if (p0 + i < pieces) tot += expf(l[i] - mx);
+        }
         L = mx + logf(tot);
         if (accumulate) acc = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow + c4) *
                               expf(la - L);
-        for (int p = 0; p < pieces; ++p)
-            acc += *reinterpret_cast<const f32x4*>(op + (size_t)p * TR * D) * expf(lp[(size_t)p * TR] - L);
+        for (int p0 = 0; p0 < pieces; p0 += OB) {
+            f32x4 ov[OB];
+            float l[OB];
+#pragma unroll
+            for (int i = 0; i < OB; ++i) {
+                const size_t pc = (size_t)min(p0 + i, pieces - 1);
+                ov[i] = *reinterpret_cast<const f32x4*>(op + pc * TR * D);
+                l[i] = lp[pc * TR];
+            }
+#pragma unroll
+            for (int i = 0; i < OB; ++i)
+                if (p0 + i < pieces) acc += ov[i] * expf(l[i] - L);
+        }
     }
     if constexpr (T == MergeOut::F32) {
         *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + c4) = acc;

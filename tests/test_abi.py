@@ -43,7 +43,8 @@ def test_header_declares_expected_entry_points():
                                          "cpattn_attn_fwd_split_plan", "cpattn_attn_fwd_workspace_size",
                                          "cpattn_attn_merge", "cpattn_qk_rmsnorm", "cpattn_ring_attn_fwd",
                                          "cpattn_status_string",
-                                         "cpattn_ulysses_pack", "cpattn_ulysses_unpack"])
+                                         "cpattn_ulysses_pack", "cpattn_ulysses_pack_n",
+                                         "cpattn_ulysses_unpack", "cpattn_ulysses_unpack_n"])
 
 
 def test_exports_every_declared_symbol(L):
@@ -57,7 +58,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.cpattn_abi_version() == _lib.ABI_VERSION == 3
+    assert L.cpattn_abi_version() == _lib.ABI_VERSION == 4
     seen = set()
     for s in range(10):
         msg = L.cpattn_status_string(s)
@@ -173,7 +174,12 @@ def piece_bytes(D):
     return 256 * (D + 1) * 4
 
 
-SCHED = 256        # bytes of dynamic-schedule counters at the head of every workspace
+SCHED = 2048       # bytes of dynamic-schedule counters at the head of every workspace
+
+
+def test_counter_area_constant():
+    m = re.search(r"#define CPATTN_WORKSPACE_COUNTER_BYTES (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == SCHED == _lib.SCHED_BYTES
 
 
 def test_split_plan(L):
@@ -265,6 +271,8 @@ def test_attn_merge_launch_size_limit(L):
 def test_relayout_row_index_limit(L):
     # more than 2^32 rows of D values do not fit the kernel's 32-bit row indices
     assert rl(L, "cpattn_ulysses_pack", src=1 << 40, dst=1 << 44, S_l=(1 << 31) - 1, H=8, P=8) == _lib.E_SHAPE
+    # a row of 2^31 or more 16-byte chunks does not fit its 32-bit chunk index within a row
+    assert rl(L, "cpattn_ulysses_pack", src=1 << 40, dst=1 << 46, B=1, S_l=1, H=8, P=8, D=1 << 34) == _lib.E_SHAPE
 
 
 def test_binding_refuses_undivided_relayout():
@@ -365,6 +373,58 @@ def test_relayout_validation(L, fn):
     assert rl(L, fn, D=4) == _lib.E_HEADDIM            # 8-byte rows
     assert rl(L, fn, dst=B_ + 8) == _lib.E_ALIGN
     assert rl(L, fn, dst=A + 1024) == _lib.E_ALIAS
+
+
+def rln(L, fn, srcs, dsts, n=None, **kw):
+    """Batched relayout with host arrays of fake device pointers (a None entry is a NULL one)."""
+    sa = (ctypes.c_void_p * max(1, len(srcs)))(*srcs)
+    da = (ctypes.c_void_p * max(1, len(dsts)))(*dsts)
+    a = dict(B=1, S_l=5520, H=24, D=128, P=8, dt=0, d=0)
+    a.update(kw)
+    return getattr(L, fn)(sa, da, len(srcs) if n is None else n, a["B"], a["S_l"], a["H"], a["D"], a["P"],
+                          a["dt"], a["d"], None)
+
+
+@pytest.mark.parametrize("fn", ["cpattn_ulysses_pack_n", "cpattn_ulysses_unpack_n"])
+def test_batched_relayout_validation(L, fn):
+    """The batched relayout checks each tensor as the single call does, plus the count and the
+    pairwise overlaps of every destination with every source and every other destination."""
+    # one shard [1, 5520, 24, 128] bf16 is 33,914,880 bytes: 1 GiB apart never overlaps
+    src = [(1 + i) << 30 for i in range(8)]
+    dst = [(16 + i) << 30 for i in range(8)]
+    gap = 33914880
+    assert getattr(L, fn)(None, (ctypes.c_void_p * 1)(dst[0]), 1, 1, 5520, 24, 128, 8, 0, 0, None) == _lib.E_NULL
+    assert getattr(L, fn)((ctypes.c_void_p * 1)(src[0]), None, 1, 1, 5520, 24, 128, 8, 0, 0, None) == _lib.E_NULL
+    assert rln(L, fn, src[:3], dst[:3], n=0) == _lib.E_SHAPE
+    assert rln(L, fn, src[:3], [dst[0], None, dst[2]]) == _lib.E_NULL
+    assert rln(L, fn, [src[0], src[1], None], dst[:3]) == _lib.E_NULL
+    assert rln(L, fn, src[:3], dst[:3], dt=3) == _lib.E_DTYPE
+    assert rln(L, fn, src[:3], dst[:3], H=20) == _lib.E_SHAPE
+    assert rln(L, fn, src[:3], dst[:3], D=4) == _lib.E_HEADDIM
+    assert rln(L, fn, src[:3], [dst[0], dst[1] + 8, dst[2]]) == _lib.E_ALIGN
+    assert rln(L, fn, src[:3], [dst[0], dst[1], src[0] + 1024]) == _lib.E_ALIAS      # dst 2 over src 0
+    assert rln(L, fn, src[:3], [dst[0], dst[0] + gap - 16, dst[2]]) == _lib.E_ALIAS  # dst 1 over dst 0
+    assert rln(L, fn, src[:3], dst[:3], S_l=(1 << 31) - 1) == _lib.E_SHAPE          # > 2^32 rows
+
+
+def test_batched_relayout_count_limit(L):
+    """More than CPATTN_MAX_RELAYOUT_TENSORS tensors is a shape error (before any pointer is read
+    past the eighth)."""
+    src = [(1 + i) << 30 for i in range(9)]
+    dst = [(16 + i) << 30 for i in range(9)]
+    assert rln(L, "cpattn_ulysses_pack_n", src, dst) == _lib.E_SHAPE
+
+
+def test_binding_refuses_mixed_batched_relayout():
+    import torch
+    import long_sequence_bidirectional_amd as cp
+    a = torch.zeros((1, 10, 8, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="first one"):
+        cp.ulysses_pack_n([a, torch.zeros((1, 11, 8, 128), dtype=torch.bfloat16)], 8, cp.SEQ_TO_HEAD)
+    with pytest.raises(ValueError, match="1 to 8"):
+        cp.ulysses_pack_n([a] * 9, 8, cp.SEQ_TO_HEAD)
+    with pytest.raises(ValueError, match="1 to 8"):
+        cp.ulysses_unpack_n([], 8, cp.SEQ_TO_HEAD)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -23,7 +23,7 @@ import torch
 
 import oracle
 import long_sequence_bidirectional_amd as cp
-from long_sequence_bidirectional_amd import inputs
+from long_sequence_bidirectional_amd import _lib, inputs
 from helpers import log
 
 pytestmark = pytest.mark.gpu
@@ -162,10 +162,13 @@ def test_fp8_dynamic_schedule_same_bits(B, H, Sq, Skv):
     log(f"case: fp8 dynamic schedule B{B} H{H} Sq{Sq} Skv{Skv}")
     q, k, v = (dev8(inputs.random_e4m3((B, H, n, 128), 7500 + i)) for i, n in enumerate((Sq, Skv, Skv)))
     ws, n = ws_fp8(B, H, Sq, Skv, 128, False)
-    assert n == 256
+    assert n == _lib.SCHED_BYTES
     o_ref, l_ref = cp.attn_fwd_fp8(q, k, v)
     for rep in range(2):
-        o, l = cp.attn_fwd_fp8(q, k, v, workspace=ws)
+        # outputs start as NaN, so a unit that no workgroup ran would show
+        o = torch.full_like(o_ref, float("nan"))
+        l = torch.full_like(l_ref, float("nan"))
+        cp.attn_fwd_fp8(q, k, v, o=o, lse=l, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(l, l_ref), rep
 

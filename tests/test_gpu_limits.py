@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import long_sequence_bidirectional_amd as cp
-from long_sequence_bidirectional_amd import inputs
+from long_sequence_bidirectional_amd import _lib, inputs
 from helpers import assert_bf16_parity, dev_bf16, f64_of_bf16, host64, log, scale_of
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -60,7 +60,7 @@ def test_q_beyond_2_31_elements():
     vb = inputs.random_bf16((1, H, Skv, D), 6102)
     q = dev_bf16(qb).repeat(1, 1, REPEAT, 1)
     n = cp.attn_fwd_workspace_size(1, H, Sq, Skv, D)
-    assert n == 256        # 24 * 4096 tiles fill whole waves: no split, only the schedule counters
+    assert n == _lib.SCHED_BYTES        # 24 * 4096 tiles fill whole waves: no split, only the schedule counters
     k, v = dev_bf16(kb), dev_bf16(vb)
     o, lse = cp.attn_fwd(q, k, v)
     # the dynamic schedule (counters in the workspace) over the same 98304 units: the same bits

@@ -19,7 +19,10 @@ def _bits(t: torch.Tensor) -> np.ndarray:
 
 @pytest.mark.parametrize("B,S_l,H,D,P,dtype", [(1, 5520, 24, 128, 8, "bf16"), (2, 37, 12, 64, 4, "bf16"),
                                                (1, 9, 6, 8, 3, "bf16"), (1, 11, 8, 4, 2, "f32"),
-                                               (1, 1, 8, 128, 8, "bf16")])
+                                               (1, 1, 8, 128, 8, "bf16"),
+                                               (1, 7, 6, 72, 3, "bf16"),      # 9 chunks of 16 B per row
+                                               (2, 5, 4, 320, 2, "bf16"),     # 40 chunks, tiles of 12 rows
+                                               (1, 3, 4, 8192, 2, "bf16")])   # 1024 chunks: a tile per row
 def test_relayout_bit_exact(B, S_l, H, D, P, dtype):
     log(f"case: relayout B{B} S_l{S_l} H{H} D{D} P{P} {dtype}")
     rng = np.random.Generator(np.random.PCG64(S_l + H))
@@ -69,3 +72,26 @@ def test_simulated_ulysses_pipeline():
     got = np.concatenate([host64(b) for b in back], axis=1)
     # LSE is not part of the pipeline's output; compare O only (pass the oracle LSE through)
     assert_bf16_parity(got, L, O_tok, L, "ulysses pipeline")
+
+
+@pytest.mark.parametrize("n", [1, 3, 8])
+@pytest.mark.parametrize("B,S_l,H,D,P", [(1, 5520, 24, 128, 8), (2, 37, 12, 64, 4), (1, 1, 8, 8, 8)])
+def test_batched_relayout_bit_exact(B, S_l, H, D, P, n):
+    """ulysses_pack_n / ulysses_unpack_n move n tensors in one launch; each result is the
+    oracle's index map of its own source, bit for bit, in both directions."""
+    log(f"case: batched relayout n={n} B{B} S_l{S_l} H{H} D{D} P{P}")
+    rng = np.random.Generator(np.random.PCG64(7000 + n * 100 + S_l))
+    shards = [rng.integers(0, 1 << 16, size=(B, S_l, H, D), dtype=np.uint16) for _ in range(n)]
+    ts = [torch.from_numpy(s.view(np.int16)).view(torch.bfloat16).cuda() for s in shards]
+    send = cp.ulysses_pack_n(ts, P, cp.SEQ_TO_HEAD)
+    heads = cp.ulysses_unpack_n(send, P, cp.SEQ_TO_HEAD)
+    send2 = cp.ulysses_pack_n(heads, P, cp.HEAD_TO_SEQ)
+    back = cp.ulysses_unpack_n(send2, P, cp.HEAD_TO_SEQ)
+    torch.cuda.synchronize()
+    for i, shard in enumerate(shards):
+        ref_send = oracle.ulysses_pack(shard, P, oracle.SEQ_TO_HEAD)
+        ref_heads = oracle.ulysses_unpack(ref_send, P, oracle.SEQ_TO_HEAD)
+        assert np.array_equal(_bits(send[i]), ref_send), i
+        assert np.array_equal(_bits(heads[i]), ref_heads), i
+        assert np.array_equal(_bits(send2[i]), oracle.ulysses_pack(ref_heads, P, oracle.HEAD_TO_SEQ)), i
+        assert np.array_equal(_bits(back[i]), shard), i

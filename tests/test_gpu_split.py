@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import long_sequence_bidirectional_amd as cp
-from long_sequence_bidirectional_amd import inputs
+from long_sequence_bidirectional_amd import _lib, inputs
 from helpers import assert_bf16_parity, dev_bf16, f64_of_bf16, host64, log, scale_of
 
 pytestmark = pytest.mark.gpu
@@ -66,7 +66,7 @@ def test_workspace_size_bounds_the_split():
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     o_ref, l_ref = cp.attn_fwd(q, k, v)
     piece = 256 * (D + 1) * 4
-    sched = 256           # schedule counters at the head of the workspace
+    sched = _lib.SCHED_BYTES   # schedule counters at the head of the workspace
     # no workspace, or room for under two pieces per tile: the unsplit kernel, bit for bit
     # (the dynamic schedule with a workspace runs the same units with the same arithmetic)
     for nbytes in (0, sched - 1, sched + 3 * piece, sched + 15 * piece + 100):
@@ -97,10 +97,13 @@ def test_dynamic_schedule_same_bits(B, H, Sq, Skv, D):
     qb, kb, vb = rand_qkv(B, H, Sq, Skv, D, 3150 + Sq)
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     ws, n = workspace(B, H, Sq, Skv, D)
-    assert n == 256, "expected the counters only (no split)"
+    assert n == _lib.SCHED_BYTES, "expected the counters only (no split)"
     o_ref, l_ref = cp.attn_fwd(q, k, v)
     for rep in range(2):
-        o, l = cp.attn_fwd_ex(q, k, v, workspace=ws)
+        # outputs start as NaN, so a unit that no workgroup ran would show
+        o = torch.full_like(o_ref, float("nan"))
+        l = torch.full_like(l_ref, float("nan"))
+        cp.attn_fwd_ex(q, k, v, o=o, lse=l, workspace=ws)
         torch.cuda.synchronize()
         assert same_bits(o, o_ref) and same_bits(l, l_ref), f"call {rep}"
 
@@ -182,3 +185,25 @@ def test_ring_driver_with_split_chunks(use_work):
     v_all = np.concatenate([vcb[c] for c in range(n)], axis=2)
     O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(k_all), f64_of_bf16(v_all), scale_of(D))
     assert_bf16_parity(host64(o), host64(l), O, L, "ring with split chunks")
+
+
+@pytest.mark.parametrize("H,Sq", [(2, 2304),       # 18 units per chunk: the shared counter only
+                                  (8, 8448)])      # 264 units: per-XCD ranges of 32 and a tail of 8
+def test_ring_driver_many_chunks(H, Sq):
+    """35 chunks: chunk c takes schedule counter set c % 16 of the work buffers, and the sets are
+    cleared once per 16 chunks (before chunks 0, 16 and 32), so later chunks reuse cleared sets."""
+    n, Skv_c, D = 35, 130, 64                      # 3 key blocks per chunk (no split)
+    log(f"case: ring n{n} Skv_c{Skv_c} H{H} Sq{Sq} D{D}")
+    qb = inputs.random_bf16((1, H, Sq, D), 3700)
+    kcb = inputs.random_bf16((n, 1, H, Skv_c, D), 3701)
+    vcb = inputs.random_bf16((n, 1, H, Skv_c, D), 3702)
+    q, kc, vc = dev_bf16(qb), dev_bf16(kcb), dev_bf16(vcb)
+    o, l = cp.ring_attn_fwd(q, kc, vc)
+    o2, l2 = cp.ring_attn_fwd(q, kc, vc, use_work=False)      # static schedule, same units
+    torch.cuda.synchronize()
+    assert same_bits(o, o2) and same_bits(l, l2)
+    k_all = np.concatenate([kcb[c] for c in range(n)], axis=2)
+    v_all = np.concatenate([vcb[c] for c in range(n)], axis=2)
+    rows = np.array([0, 1, 255, 256, 1000, 2303, Sq - 1])
+    O, L = oracle.attention_rows(f64_of_bf16(qb), f64_of_bf16(k_all), f64_of_bf16(v_all), scale_of(D), rows)
+    assert_bf16_parity(host64(o[:, :, rows]), host64(l[:, :, rows]), O, L, "ring over 35 chunks")
