@@ -35,14 +35,15 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_CLOCK_MHZ = 2400.0     # engine clock the matrix-core peak is quoted at
 LAYERS = 36
 KERNEL_SRC = [os.path.join(ROOT, "long_sequence_bidirectional_amd", "csrc", f)
-              for f in ("attn_fwd_kernel.h", "attn_fwd_bf16.hip")]
+              for f in ("attn_fwd_kernel.h", "attn_fwd_bf16.hip", "unit_sched.h", "kernels.h", "common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_video_layer_traffic.json")
 # calibration copy for the HBM counters: Ulysses pack of a [44160, 24, 128] bf16 shard
 CALIB_SHAPE = (1, 44160, 24, 128)
 
 
 def kernel_source_hash() -> str:
-    """SHA-256 over the sources of the bf16 attention kernel (template and instantiation)."""
+    """SHA-256 over the sources of the bf16 attention kernel (template, instantiation, unit
+    schedule and the shared headers)."""
     import hashlib
     h = hashlib.sha256()
     for path in KERNEL_SRC:
