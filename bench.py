@@ -331,6 +331,10 @@ def profile_pass(cp, torch, q, k, v):
     for a, b in zip(shards, sends):
         cp.ulysses_unpack(b, P, cp.SEQ_TO_HEAD, dst=a.view(1, H // P, S_L * P, D))
     torch.cuda.synchronize()
+    # the same shards as 4 batched packs of three (one rank's Q, K, V per launch)
+    for i in range(0, 12, 3):
+        cp.ulysses_pack_n(shards[i:i + 3], P, cp.SEQ_TO_HEAD, dsts=sends[i:i + 3])
+    torch.cuda.synchronize()
     del shards, sends
     # the fp8 self-attention (E4M3 of N(0,1) draws, made on the device) and the QK-RMSNorm
     # prologue over the attention sample's K [56320, 32, 128] fp16 (461 MB each way)
@@ -351,7 +355,8 @@ def profile_pass(cp, torch, q, k, v):
     cp.qk_rmsnorm(x, w, 1e-6, D ** -0.25, out=y)
     torch.cuda.synchronize()
     print(f"profile pass done; calibration copy {CALIB_SHAPE[1] * CALIB_SHAPE[2] * CALIB_SHAPE[3] * 2} bytes "
-          "read and written; 12 cold merges, packs and unpacks; fp8 self-attention; QK-RMSNorm of "
+          "read and written; 12 cold merges, packs and unpacks; 4 batched packs of 3 shards; fp8 "
+          "self-attention; QK-RMSNorm of "
           f"{x.numel() * 2} bytes", flush=True)
 
 
