@@ -354,10 +354,15 @@ def profile_pass(cp, torch, q, k, v):
     torch.cuda.synchronize()
     cp.qk_rmsnorm(x, w, 1e-6, D ** -0.25, out=y)
     torch.cuda.synchronize()
+    norm_bytes = x.numel() * 2
+    del x, w, y
+    # the bf16 self-attention again with K stored sequence-last [1,24,128,44160]
+    kt = k.transpose(2, 3).contiguous()
+    cp.attn_fwd_ex(q, kt, v, o=o, lse=l, workspace=workspace(cp, torch, B, H, S, k.shape[2], D), k_seq_last=True)
+    torch.cuda.synchronize()
     print(f"profile pass done; calibration copy {CALIB_SHAPE[1] * CALIB_SHAPE[2] * CALIB_SHAPE[3] * 2} bytes "
           "read and written; 12 cold merges, packs and unpacks; 4 batched packs of 3 shards; fp8 "
-          "self-attention; QK-RMSNorm of "
-          f"{x.numel() * 2} bytes", flush=True)
+          f"self-attention; QK-RMSNorm of {norm_bytes} bytes; self-attention with K sequence-last", flush=True)
 
 
 def timed_leg(torch, stream, fn, flops=None, nbytes=None, iters=50, warmup=3, clock=True):
@@ -550,6 +555,16 @@ def secondary_rows(cp, torch, q, k, v, stream, kt=None, vt=None):
     out.update(cold_rows(cp, torch, stream))
     out.update(p4_rows(cp, torch, stream))
     out.update(fp8_rows(cp, torch, stream))
+    # self-attention S=44160 with K stored sequence-last ([1,24,128,44160], the attention sample's
+    # hint-file layout for K), Q, V, O head-major, its planned workspace
+    kt_ = k.transpose(2, 3).contiguous()
+    o_kt = torch.empty_like(q)
+    l_kt = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    ws_kt = workspace(cp, torch, 1, H, inputs.S_VIDEO, inputs.S_VIDEO, D)
+    out["self_k_seq_last"] = timed_leg(
+        torch, stream, lambda: cp.attn_fwd_ex(q, kt_, v, o=o_kt, lse=l_kt, workspace=ws_kt, k_seq_last=True,
+                                              stream=stream), 4.0 * H * inputs.S_VIDEO ** 2 * D, iters=20)
+    del kt_, o_kt, l_kt, ws_kt
     return out
 
 

@@ -101,6 +101,7 @@ typedef enum {
 /* Flags of cpattn_attn_fwd_ex. */
 #define CPATTN_FLAG_ACCUMULATE 1u
 #define CPATTN_FLAG_SEQ_MAJOR 2u
+#define CPATTN_FLAG_K_SEQ_LAST 4u
 
 /* CPATTN_E4M3 (OCP FP8 E4M3 bytes) is only an in_dtype of cpattn_attn_fwd_workspace_size:
  * cpattn_attn_fwd_fp8 takes no dtype for its inputs. */
@@ -148,8 +149,9 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
  *                    ignored and undefined on return.  Must not overlap any
  *                    tensor argument (CPATTN_E_ALIAS); NULL with a nonzero
  *                    size is CPATTN_E_NULL.
- *   flags            any of CPATTN_FLAG_ACCUMULATE, CPATTN_FLAG_SEQ_MAJOR; other
- *                    bits -> CPATTN_E_FLAGS.
+ *   flags            any of CPATTN_FLAG_ACCUMULATE, CPATTN_FLAG_SEQ_MAJOR,
+ *                    CPATTN_FLAG_K_SEQ_LAST (not together with SEQ_MAJOR);
+ *                    other bits or that pair -> CPATTN_E_FLAGS.
  *
  * Workspace.  The bf16 kernel runs 256 query rows of one (b, h) per
  * workgroup, at most one workgroup per resident slot, each looping over
@@ -189,6 +191,15 @@ cpattn_status cpattn_attn_fwd(const void* q, const void* k, const void* v, void*
  * all-to-all, so no relayout pass is needed on the head side.  Same results
  * as the head-major call on the transposed tensors, bit for bit.  A token
  * row (H * D elements) must be shorter than 2^25 elements (CPATTN_E_SHAPE).
+ *
+ * CPATTN_FLAG_K_SEQ_LAST.  k is [B, H, D, Skv]: each head's keys stored with
+ * the sequence last, the layout the attention sample's sharding hint gives
+ * K (K of rank 4 with its sequence at dimension 3, "TensorRT multi-device
+ * attention inference in practice", the hint-file section); q, v and o stay
+ * head-major [B, H, S, D].  The same arithmetic on the same tiles as with
+ * k [B, H, Skv, D], so the same results, bit for bit.  Requires BF16 or F16
+ * inputs (CPATTN_E_DTYPE), Skv a multiple of 8 and D * Skv * 2 < 2^32
+ * (CPATTN_E_SHAPE).
  */
 cpattn_status cpattn_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t D,

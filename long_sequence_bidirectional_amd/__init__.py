@@ -23,7 +23,8 @@ from __future__ import annotations
 import ctypes
 import math
 
-from ._lib import (BF16, E4M3, F16, F32, FLAG_ACCUMULATE, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD, STATIC_SCRATCH_BYTES,
+from ._lib import (BF16, E4M3, F16, F32, FLAG_ACCUMULATE, FLAG_K_SEQ_LAST, FLAG_SEQ_MAJOR, HEAD_TO_SEQ, SEQ_TO_HEAD,
+                   STATIC_SCRATCH_BYTES,
                    CpattnError, check, lib)
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_ex_static", "attn_fwd_workspace_size", "attn_fwd_split_plan", "attn_merge",
@@ -66,19 +67,23 @@ def _stream(stream):
     return s.cuda_stream
 
 
-def _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major=False):
+def _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major=False, k_seq_last=False):
     """Shapes, defaults and the C argument tuple of an attention call.  Head-major tensors are
-    [B, H, S, D]; sequence-major ones [B, S, H, D]; lse is [B, H, Sq] either way."""
+    [B, H, S, D]; sequence-major ones [B, S, H, D]; with k_seq_last k is [B, H, D, Skv]; lse is
+    [B, H, Sq] in every layout."""
     torch = _torch()
+    if seq_major and k_seq_last:
+        raise ValueError("k_seq_last takes head-major q, v and o")
     if seq_major:
         B, Sq, H, D = q.shape
         Skv = k.shape[1]
         kv_shape, o_shape = (B, Skv, H, D), (B, Sq, H, D)
     else:
         B, H, Sq, D = q.shape
-        Skv = k.shape[2]
+        Skv = v.shape[2]
         kv_shape, o_shape = (B, H, Skv, D), (B, H, Sq, D)
-    if tuple(k.shape) != kv_shape or v.shape != k.shape:
+    k_shape = (B, H, D, Skv) if k_seq_last else kv_shape
+    if tuple(k.shape) != k_shape or tuple(v.shape) != kv_shape:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
@@ -104,17 +109,19 @@ def attn_fwd(q, k, v, o=None, lse=None, scale=None, out_dtype=None, stream=None)
 
 
 def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, out_dtype=None, workspace=None, accumulate=False,
-                seq_major=False, stream=None):
+                seq_major=False, stream=None, k_seq_last=False):
     """attn_fwd with a workspace (uint8 device tensor, key-range split of the last wave), an
-    accumulate mode that folds the result into the f32 (o, lse) already there, and a
-    sequence-major layout (q [B,Sq,H,D], k/v [B,Skv,H,D], o [B,Sq,H,D])."""
+    accumulate mode that folds the result into the f32 (o, lse) already there, a
+    sequence-major layout (q [B,Sq,H,D], k/v [B,Skv,H,D], o [B,Sq,H,D]) and a sequence-last K
+    (k_seq_last: k [B,H,D,Skv] with head-major q, v, o; Skv a multiple of 8)."""
     if accumulate and (o is None or lse is None):
         raise ValueError("accumulate needs the existing o and lse")
-    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major)
+    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major, k_seq_last)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None and workspace.numel() > 0:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    flags = (FLAG_ACCUMULATE if accumulate else 0) | (FLAG_SEQ_MAJOR if seq_major else 0)
+    flags = ((FLAG_ACCUMULATE if accumulate else 0) | (FLAG_SEQ_MAJOR if seq_major else 0)
+             | (FLAG_K_SEQ_LAST if k_seq_last else 0))
     check("cpattn_attn_fwd_ex", lib().cpattn_attn_fwd_ex(*args, flags, ws_ptr, ws_bytes, _stream(stream)))
     return o, lse
 

@@ -20,6 +20,7 @@ STATIC_SCRATCH_BYTES = 32 << 20     # CPATTN_STATIC_SCRATCH_BYTES
 SCHED_BYTES = 2048                  # CPATTN_WORKSPACE_COUNTER_BYTES
 FLAG_ACCUMULATE = 1
 FLAG_SEQ_MAJOR = 2
+FLAG_K_SEQ_LAST = 4
 
 STATUS_NAMES = {OK: "OK", E_NULL: "E_NULL", E_SHAPE: "E_SHAPE", E_DTYPE: "E_DTYPE", E_HEADDIM: "E_HEADDIM",
                 E_ALIGN: "E_ALIGN", E_ALIAS: "E_ALIAS", E_HIP: "E_HIP", E_SCALE: "E_SCALE",

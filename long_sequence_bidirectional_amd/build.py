@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libcpattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_fwd_f32.hip", "attn_fwd_fp8.hip", "merge.hip", "relayout.hip",
-           "qk_norm.hip"]
+SOURCES = ["api.hip", "attn_fwd_bf16.hip", "attn_fwd_f16.hip", "attn_fwd_bf16_kt.hip", "attn_fwd_f16_kt.hip",
+           "attn_fwd_f32.hip", "attn_fwd_fp8.hip", "merge.hip", "relayout.hip", "qk_norm.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared", "-fvisibility=hidden",

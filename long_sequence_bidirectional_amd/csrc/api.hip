@@ -181,7 +181,8 @@ cpattn::Strides layout_strides(int64_t H, int64_t S, int64_t D, bool seq_major) 
 cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                        int64_t Sq, int64_t Skv, int64_t D, float scale, cpattn_dtype in_dtype, cpattn_dtype o_dtype,
                        bool accumulate, bool seq_major, float* ws_o, float* ws_lse, int64_t ws_pieces,
-                       unsigned long long* sched, unsigned long long* sched_clear, hipStream_t stream) {
+                       unsigned long long* sched, unsigned long long* sched_clear, hipStream_t stream,
+                       bool k_seq_last = false) {
     const int64_t BH = B * H;
     if (Skv == 0) {   // empty key set: O = 0, LSE = -inf, the identity of the fold
         if (accumulate) return CPATTN_OK;
@@ -196,6 +197,7 @@ cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, flo
     a.BH = BH;
     a.H = H;
     a.seq_major = seq_major;
+    a.k_seq_last = k_seq_last;
     a.sq = layout_strides(H, Sq, D, seq_major);
     a.skv = layout_strides(H, Skv, D, seq_major);
     a.so = a.sq;
@@ -224,6 +226,9 @@ cpattn_status run_attn(const void* q, const void* k, const void* v, void* o, flo
             a.ws_lse = ws_lse;
         }
     }
+    if (k_seq_last)
+        return hip_status(in_dtype == CPATTN_F16 ? cpattn::launch_attn_fwd_f16_kt(a)
+                                                 : cpattn::launch_attn_fwd_bf16_kt(a));
     return hip_status(in_dtype == CPATTN_F16 ? cpattn::launch_attn_fwd_f16(a) : cpattn::launch_attn_fwd_bf16(a));
 }
 
@@ -276,14 +281,22 @@ namespace {
 cpattn_status check_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                                 int64_t H, int64_t Sq, int64_t Skv, int64_t D, float scale, int idt, int odt,
                                 uint32_t flags, AttnFwdCheck* ck) {
-    if ((flags & ~(uint32_t)(CPATTN_FLAG_ACCUMULATE | CPATTN_FLAG_SEQ_MAJOR)) != 0) return CPATTN_E_FLAGS;
+    if ((flags & ~(uint32_t)(CPATTN_FLAG_ACCUMULATE | CPATTN_FLAG_SEQ_MAJOR | CPATTN_FLAG_K_SEQ_LAST)) != 0)
+        return CPATTN_E_FLAGS;
     const bool acc = (flags & CPATTN_FLAG_ACCUMULATE) != 0;
     const bool seq_major = (flags & CPATTN_FLAG_SEQ_MAJOR) != 0;
+    const bool k_last = (flags & CPATTN_FLAG_K_SEQ_LAST) != 0;
+    if (seq_major && k_last) return CPATTN_E_FLAGS;
     const cpattn_status st = check_attn_fwd(q, k, v, o, lse, B, H, Sq, Skv, D, scale, idt, odt, ck);
     if (st != CPATTN_OK) return st;
     if (acc && (!dtype_16bit(idt) || odt != CPATTN_F32)) return CPATTN_E_DTYPE;
     // the 16-bit kernels address a 64-row K/V block with 32-bit byte offsets
     if (seq_major && H * D >= (int64_t(1) << 25)) return CPATTN_E_SHAPE;
+    if (k_last) {
+        if (!dtype_16bit(idt)) return CPATTN_E_DTYPE;
+        // K rows of Skv keys, read in 16-byte chunks of 8 keys from offsets below 2^32 bytes
+        if (Skv % 8 != 0 || D * Skv * 2 >= (int64_t(1) << 32)) return CPATTN_E_SHAPE;
+    }
     return CPATTN_OK;
 }
 
@@ -303,7 +316,8 @@ cpattn_status run_attn_fwd_ex(const void* q, const void* k, const void* v, void*
     }
     return run_attn(q, k, v, o, lse, B, H, Sq, Skv, D, scale, static_cast<cpattn_dtype>(idt),
                     static_cast<cpattn_dtype>(odt), (flags & CPATTN_FLAG_ACCUMULATE) != 0,
-                    (flags & CPATTN_FLAG_SEQ_MAJOR) != 0, ws_o, ws_lse, ws_pieces, sched, sched, stream);
+                    (flags & CPATTN_FLAG_SEQ_MAJOR) != 0, ws_o, ws_lse, ws_pieces, sched, sched, stream,
+                    (flags & CPATTN_FLAG_K_SEQ_LAST) != 0);
 }
 
 }  // namespace

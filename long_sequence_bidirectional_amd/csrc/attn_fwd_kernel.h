@@ -116,6 +116,10 @@ __device__ __forceinline__ int swz_v(int r) {     // V: 4 consecutive rows x 4 c
     constexpr int RPB = 256 / (2 * D);
     return 4 * ((r / RPB) % (D / 32));
 }
+// K with the sequence last ([D, keys] per head): the LDS tile holds D rows of one 64-key
+// block (128 bytes each, two per 256-byte bank row); a transposing read covers 4 consecutive
+// rows x 4 chunks, so rows r and r + 2 take opposite halves of the row's 8 chunks.
+__device__ __forceinline__ int swz_kt(int r) { return ((r >> 1) & 1) << 2; }
 
 // One v_mfma_f32_32x32x16 of the input type: D(32x32) += A(32x16) B(16x32).
 template <bool F16>
@@ -145,7 +149,7 @@ __device__ __forceinline__ uint32_t pack16x2(float lo, float hi) {
 // counter a few blocks before the end of this one, so the atomic's latency overlaps the last
 // blocks; the claim is passed to every wave through *next_lds after the epilogue and returned
 // (-1 without a dynamic schedule).
-template <int D, bool F16, bool OUT_F32, bool SEQ>
+template <int D, bool F16, bool OUT_F32, bool SEQ, bool KT>
 __device__ __forceinline__ int attn_unit(
     int k_unit, bool first, int static_next, u32x4 (&qreg)[D / 16], const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse,
@@ -178,7 +182,11 @@ __device__ __forceinline__ int attn_unit(
     const int group = wave >> 2;            // waves w and w+4 share a SIMD
 
     // Row strides: D for head-major operands (compile time), runtime for sequence-major ones.
+    // KT: K is [D, keys] per head (sequence last; Q, V and O head-major): a block of keys is
+    // a column range, block j starting j * BN elements in, its rows Skv_all elements apart.
     const int64_t q_row = SEQ ? sq.row : D, kv_row = SEQ ? skv.row : D, o_row = SEQ ? so.row : D;
+    const int64_t kt_row = Skv_all;                   // (KT) row stride of K
+    const int64_t k_blk = KT ? (int64_t)BN : (int64_t)BN * kv_row;   // elements from block j to j+1
 
     // Where a work unit's data lives: its query tile, key range and output rows.
     struct Geom {
@@ -206,12 +214,11 @@ __device__ __forceinline__ int attn_unit(
         const int qt = tile - bh * nQt;
         const int b = SEQ ? bh / H : 0, h = SEQ ? bh - b * H : 0;
         const int64_t q_base = SEQ ? b * sq.batch + h * sq.head : (int64_t)bh * Sq * D;
-        const int64_t kv_off =
-            (SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv_all * D) + (int64_t)kb0 * BN * kv_row;
+        const int64_t kv_head = SEQ ? b * skv.batch + h * skv.head : (int64_t)bh * Skv_all * D;
         Geom g;
         g.qp = q + q_base;
-        g.kp = k + kv_off;
-        g.vp = v + kv_off;
+        g.kp = k + kv_head + (int64_t)kb0 * k_blk;
+        g.vp = v + kv_head + (int64_t)kb0 * BN * kv_row;
         g.o_base = SEQ ? b * so.batch + h * so.head : (int64_t)bh * Sq * D;
         g.bh = bh;
         g.qrow = qt * kBM + wave * 32 + l32;
@@ -231,11 +238,18 @@ __device__ __forceinline__ int attn_unit(
     // pieces of a block; the per-lane byte offsets within a full block are constant, so a load
     // is the block's (wave-uniform) base in SGPRs plus a fixed VGPR offset and no address
     // arithmetic runs per block.  The last, partial block clamps rows to the last valid one.
+    // (KT: a K piece is 8 of the tile's D rows of 128 bytes; lane i fills chunk i % 8 of row i / 8)
+    constexpr int KT_NC = BN / 8;           // 16-byte chunks per row of the K^T tile
     uint32_t koffb[LOADS_PER_WAVE], voffb[LOADS_PER_WAVE];
 #pragma unroll
     for (int I = 0; I < LOADS_PER_WAVE; ++I) {
         const int row = (wave_u * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
-        koffb[I] = (uint32_t)((row * kv_row + (((lane % NC) ^ swz_k<D>(row)) * 8)) * 2);
+        if constexpr (KT) {
+            const int trow = (wave_u * LOADS_PER_WAVE + I) * (1024 / (2 * BN)) + lane / KT_NC;
+            koffb[I] = (uint32_t)(((int64_t)trow * kt_row + (((lane % KT_NC) ^ swz_kt(trow)) * 8)) * 2);
+        } else {
+            koffb[I] = (uint32_t)((row * kv_row + (((lane % NC) ^ swz_k<D>(row)) * 8)) * 2);
+        }
         voffb[I] = (uint32_t)((row * kv_row + (((lane % NC) ^ swz_v<D>(row)) * 8)) * 2);
     }
     // One 1 KB piece: global address sb + off + I*1024 -> LDS lds + I*1024 + 16*lane.  M0 holds
@@ -249,13 +263,19 @@ __device__ __forceinline__ int attn_unit(
                      :: "v"(off), "s"(sb), "s"(lds), "n"(I * 1024) : "memory", "m0");
 #pragma clang diagnostic pop
     };
-    // (skv: the unit's key count; the last, partial block clamps its rows to the last key)
+    // (skv: the unit's key count; the last, partial block clamps its rows to the last key, or
+    // with KT its 8-key chunks to the last valid chunk: the key count is a multiple of 8 there)
     auto load_piece = [&]<int I>(ic<I>, const uint16_t* src, uint16_t* dst, int j, bool is_v, int skv_u) CPATTN_AI {
         const uint32_t lds = (uint32_t)(uintptr_t)LDS_PTR(void, dst + wave_u * LOADS_PER_WAVE * 512);
-        const char* blk = reinterpret_cast<const char*>(src + (int64_t)j * BN * kv_row);
+        const char* blk = reinterpret_cast<const char*>(src + (int64_t)j * (is_v ? (int64_t)BN * kv_row : k_blk));
         if ((j + 1) * BN <= skv_u) {
             if (is_v) dma(ic<I>{}, voffb[I], blk, lds);
             else dma(ic<I>{}, koffb[I], blk, lds);
+        } else if (KT && !is_v) {
+            // the lane fills position lane % 8 of its row, which holds chunk (lane % 8) ^ swz
+            const int trow = (wave_u * LOADS_PER_WAVE + I) * (1024 / (2 * BN)) + lane / KT_NC;
+            const int ch = min((lane % KT_NC) ^ swz_kt(trow), (skv_u - j * BN) / 8 - 1);
+            dma(ic<I>{}, (uint32_t)(((int64_t)trow * kt_row + ch * 8) * 2), blk, lds);
         } else {
             const int row = (wave_u * LOADS_PER_WAVE + I) * ROWS_PER_LOAD + lane / NC;
             const int ch = (lane % NC) ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
@@ -296,9 +316,22 @@ __device__ __forceinline__ int attn_unit(
     };
 
     // ---- LDS read addresses: lane-dependent parts (elements); the rest folds into offsets
-    int koff[NKS], voff[NDT];
+    int koff[KT ? 1 : NKS], voff[NDT], kofft[KT ? NKT : 1];
+    if constexpr (KT) {
+        // K^T tile, transposing reads: lane (L16, g16, hh) addresses row 16 ks + 8 hh + 4 h2 +
+        // L16 / 4 and columns (keys) 32 kt + 16 g16 + 4 (L16 % 4) .. + 3, and receives rows
+        // r0 .. r0 + 3 of column 32 kt + l32: four consecutive head-dim values of its key, so two
+        // reads give the same 8 values per lane as the row-major K fragment
+        const int rowl = 8 * hh + (L16 >> 2);            // swz_kt depends on bit 1 of the row only
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * D + (((2 * ks + hh) ^ swz_k<D>(l32)) * 8);
+        for (int kt = 0; kt < NKT; ++kt) {
+            const int col = kt * 32 + 16 * g16 + 4 * (L16 & 3);
+            kofft[kt] = rowl * BN + (((col >> 3) ^ swz_kt(rowl)) * 8) + (col & 7);
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * D + (((2 * ks + hh) ^ swz_k<D>(l32)) * 8);
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
         const int col = dt * 32 + 16 * g16 + 4 * (L16 & 3);
@@ -306,7 +339,17 @@ __device__ __forceinline__ int attn_unit(
         voff[dt] = row * D + (((col >> 3) ^ swz_v<D>(row)) * 8) + ((col >> 2) & 1) * 4;
     }
     auto read_k = [&]<int BUF>(ic<BUF>, int kt, int ks) CPATTN_AI -> u32x4 {
-        return *reinterpret_cast<const u32x4*>(&Ks[BUF][kt * 32 * D + koff[ks]]);
+        if constexpr (KT) {
+            i16x4 r[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    LDS_PTR(i16x4, &Ks[BUF][(16 * ks + 4 * h2) * BN + kofft[kt]]));
+            const u32x2 a0 = __builtin_bit_cast(u32x2, r[0]), a1 = __builtin_bit_cast(u32x2, r[1]);
+            return u32x4{a0[0], a0[1], a1[0], a1[1]};
+        } else {
+            return *reinterpret_cast<const u32x4*>(&Ks[BUF][kt * 32 * D + koff[ks]]);
+        }
     };
     auto read_vt = [&]<int BUF>(ic<BUF>, int dt, int t) CPATTN_AI -> u32x4 {
         i16x4 r[2];
@@ -390,7 +433,7 @@ __device__ __forceinline__ int attn_unit(
     auto issue_part = [&]<int R, int P, bool FULL>(ic<R>, ic<P>, std::bool_constant<FULL>, int j) CPATTN_AI {
         if constexpr (P < LOADS_PER_WAVE) {
             if constexpr (FULL) {
-                dma(ic<P>{}, koffb[P], reinterpret_cast<const char*>(kp + (int64_t)(j + 3) * BN * kv_row),
+                dma(ic<P>{}, koffb[P], reinterpret_cast<const char*>(kp + (int64_t)(j + 3) * k_blk),
                     (uint32_t)(uintptr_t)LDS_PTR(void, Ks[(R + 3) % 4] + wave_u * LOADS_PER_WAVE * 512));
             } else {
                 if (j + 3 < nblk) load_piece(ic<P>{}, kp, Ks[(R + 3) % 4], j + 3, false, Skv);
@@ -690,7 +733,7 @@ __device__ __forceinline__ int attn_unit(
 // its L2.
 //
 // Dynamic schedule (map.sched): per-XCD ranges of units with a shared tail (unit_sched.h).
-template <int D, bool F16, bool OUT_F32, bool SEQ>
+template <int D, bool F16, bool OUT_F32, bool SEQ, bool KT>
 __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, float* __restrict__ lse, int Sq, int Skv_all, int nQt, int H, Strides sq, Strides skv,
@@ -721,7 +764,7 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     bool first = true;
     while (u >= 0 && u < n_units) {       // one call site: the unit body is inlined once
         const int after = dynamic ? -1 : next_static();
-        u = attn_unit<D, F16, OUT_F32, SEQ>(u, first, after, qreg, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv,
+        u = attn_unit<D, F16, OUT_F32, SEQ, KT>(u, first, after, qreg, q, k, v, o, lse, Sq, Skv_all, nQt, H, sq, skv,
                                             so, map, c, &next_unit);
         first = false;
     }
@@ -732,7 +775,7 @@ __global__ void zero_sched_kernel(unsigned long long* sched) {
     for (int i = threadIdx.x; i < kSchedWords; i += blockDim.x) sched[i] = 0;
 }
 
-template <int D, bool F16, bool OUT_F32, bool SEQ>
+template <int D, bool F16, bool OUT_F32, bool SEQ, bool KT>
 hipError_t launch(const AttnFwdArgs& a) {
     const int nQt = (int)((a.Sq + kBM - 1) / kBM);
     const int64_t total = (int64_t)a.BH * nQt;
@@ -757,7 +800,7 @@ hipError_t launch(const AttnFwdArgs& a) {
         const hipError_t ez = hipGetLastError();
         if (ez != hipSuccess) return ez;
     }
-    hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, F16, OUT_F32, SEQ>), dim3(launch_grid), dim3(512), 0, a.stream,
+    hipLaunchKernelGGL((attn_fwd_mfma_kernel<D, F16, OUT_F32, SEQ, KT>), dim3(launch_grid), dim3(512), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), a.o, a.lse, (int)a.Sq, (int)a.Skv, nQt, (int)a.H, a.sq,
                        a.skv, a.so, m, c, grid);
@@ -771,7 +814,7 @@ hipError_t launch(const AttnFwdArgs& a) {
 template <int D, bool F16, bool OUT_F32>
 int occupancy() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_mfma_kernel<D, F16, OUT_F32, false>, 512, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_mfma_kernel<D, F16, OUT_F32, false, false>, 512, 0) !=
         hipSuccess)
         return 0;
     return n;
@@ -779,13 +822,22 @@ int occupancy() {
 
 template <int D, bool F16, bool OUT_F32>
 hipError_t launch_layout(const AttnFwdArgs& a) {
-    return a.seq_major ? launch<D, F16, OUT_F32, true>(a) : launch<D, F16, OUT_F32, false>(a);
+    return a.seq_major ? launch<D, F16, OUT_F32, true, false>(a) : launch<D, F16, OUT_F32, false, false>(a);
 }
 
+// Q, K, V and O head-major or sequence-major (the K-sequence-last layout has units of its own).
 template <bool F16>
 hipError_t launch_any(const AttnFwdArgs& a) {
     if (a.D == 128) return a.out_f32 ? launch_layout<128, F16, true>(a) : launch_layout<128, F16, false>(a);
     return a.out_f32 ? launch_layout<64, F16, true>(a) : launch_layout<64, F16, false>(a);
+}
+
+// K [B, H, D, Skv] (sequence last), Q, V and O head-major.
+template <bool F16>
+hipError_t launch_kt(const AttnFwdArgs& a) {
+    if (a.D == 128)
+        return a.out_f32 ? launch<128, F16, true, false, true>(a) : launch<128, F16, false, false, true>(a);
+    return a.out_f32 ? launch<64, F16, true, false, true>(a) : launch<64, F16, false, false, true>(a);
 }
 
 }  // namespace

@@ -26,6 +26,7 @@ struct AttnFwdArgs {
     int64_t BH;      // B * H
     int64_t H;
     bool seq_major;        // operands [B,S,H,D] (else [B,H,S,D]); the strides below agree
+    bool k_seq_last;       // k is [B,H,D,Skv] (q, v, o head-major; 16-bit inputs, Skv % 8 == 0)
     Strides sq, skv, so;   // of q, of k and v, of o (lse is always [B, H, Sq])
     int64_t Sq;
     int64_t Skv;     // >= 1 (Skv == 0 is handled by launch_fill_empty)
@@ -88,6 +89,8 @@ inline int sched_per_xcd(int64_t n_dp, int64_t G) {
 
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f16(const AttnFwdArgs& a);
+hipError_t launch_attn_fwd_bf16_kt(const AttnFwdArgs& a);   // a.k_seq_last
+hipError_t launch_attn_fwd_f16_kt(const AttnFwdArgs& a);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs& a);
 
 // Attention with OCP FP8 E4M3 inputs (D = 128), one f32 scale per tensor.  Work split,

@@ -117,7 +117,7 @@ def test_attn_fwd_ex_validation(L):
     assert fwd_ex(L, scale=0.0) == _lib.E_SCALE
     assert fwd_ex(L, o=A + 16) == _lib.E_ALIAS
     # flags
-    assert fwd_ex(L, flags=4) == _lib.E_FLAGS
+    assert fwd_ex(L, flags=8) == _lib.E_FLAGS
     assert fwd_ex(L, flags=_lib.FLAG_SEQ_MAJOR | 8) == _lib.E_FLAGS
     assert fwd_ex(L, flags=0x80000000) == _lib.E_FLAGS
     # the layout flag keeps every other check
@@ -143,6 +143,33 @@ def fwd_static(L, q=A, k=B_, v=C, o=D_, lse=E, B=1, H=2, Sq=256, Skv=256, D=64, 
     return L.cpattn_attn_fwd_ex_static(q, k, v, o, lse, B, H, Sq, Skv, D, scale, i, od, flags, nbytes, None)
 
 
+def test_k_seq_last_validation(L):
+    """CPATTN_FLAG_K_SEQ_LAST: 16-bit inputs only, not with the sequence-major layout, Skv a
+    multiple of 8 and D * Skv * 2 below 2^32; the fp8 entry point does not take the flag."""
+    KT = 4
+    def ex(flags, i=0, od=0, Skv=256, D=64, q=A, k=B_, v=C, o=D_, lse=E):
+        return L.cpattn_attn_fwd_ex(q, k, v, o, lse, 1, 2, 256, Skv, D, 0.125, i, od, flags, None, 0, None)
+    assert ex(KT | 2) == _lib.E_FLAGS
+    assert ex(KT, i=_lib.F32, od=_lib.F32) == _lib.E_DTYPE
+    assert ex(KT, Skv=260) == _lib.E_SHAPE
+    far = [(i + 1) << 44 for i in range(5)]
+    assert ex(KT, Skv=1 << 24, D=128, q=far[0], k=far[1], v=far[2], o=far[3], lse=far[4]) == _lib.E_SHAPE
+    assert ex(8) == _lib.E_FLAGS
+    assert L.cpattn_attn_fwd_fp8(A, B_, C, D_, E, 1, 2, 256, 256, 128, 0.1, 1.0, 1.0, 1.0, 0, KT, None, 0,
+                                 None) == _lib.E_FLAGS
+
+
+def test_binding_k_seq_last_shapes():
+    import torch
+    import long_sequence_bidirectional_amd as cp
+    q = torch.zeros((1, 2, 16, 64), dtype=torch.bfloat16)
+    v = torch.zeros((1, 2, 24, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape mismatch"):
+        cp.attn_fwd_ex(q, torch.zeros((1, 2, 24, 64), dtype=torch.bfloat16), v, k_seq_last=True)
+    with pytest.raises(ValueError, match="head-major"):
+        cp.attn_fwd_ex(q, torch.zeros((1, 2, 64, 24), dtype=torch.bfloat16), v, seq_major=True, k_seq_last=True)
+
+
 def test_attn_fwd_ex_static_validation(L):
     """Every check of attn_fwd_ex except the workspace pointer's, plus the scratch limit; all of
     them run before the one HIP call (the lookup of the scratch's device address)."""
@@ -157,7 +184,7 @@ def test_attn_fwd_ex_static_validation(L):
     assert fwd_static(L, D=96) == _lib.E_HEADDIM
     assert fwd_static(L, scale=float("nan")) == _lib.E_SCALE
     assert fwd_static(L, o=A + 16) == _lib.E_ALIAS
-    assert fwd_static(L, flags=4) == _lib.E_FLAGS
+    assert fwd_static(L, flags=8) == _lib.E_FLAGS
     assert fwd_static(L, flags=_lib.FLAG_ACCUMULATE, od=_lib.BF16) == _lib.E_DTYPE
     assert fwd_static(L, flags=_lib.FLAG_SEQ_MAJOR, H=1 << 19, Sq=1, Skv=1) == _lib.E_SHAPE
 

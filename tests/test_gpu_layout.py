@@ -143,3 +143,83 @@ def test_ulysses_fused_small():
     err = np.abs(host64(o.transpose(1, 2)) - O)
     log(f"  fused Ulysses vs oracle: O max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+KT_SHAPES = [
+    (1, 3, 300, 328, 128),    # ragged Q tail; 5 full key blocks + 8 keys
+    (2, 2, 513, 704, 64),     # batch 2, D = 64, 11 full blocks
+    (1, 4, 17, 2992, 128),    # the text-token count (46 blocks + 48 keys)
+    (1, 2, 256, 8, 128),      # one partial block of 8 keys
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("out_f32", [False, True], ids=["o_16", "o_f32"])
+@pytest.mark.parametrize("B,H,Sq,Skv,D", KT_SHAPES)
+def test_k_seq_last_equals_head_major(B, H, Sq, Skv, D, out_f32, dtype):
+    """K given as [B, H, D, Skv] (sequence last, the sample's hint-file layout) runs the same
+    arithmetic on the same tiles as K [B, H, Skv, D]: the same bits, and the oracle's result."""
+    log(f"case: K sequence-last B{B} H{H} Sq{Sq} Skv{Skv} D{D} {dtype} out_f32={out_f32}")
+    seed = 4400 + Sq + Skv + D
+    qb = inputs.random_bf16((B, H, Sq, D), seed)
+    kb = inputs.random_bf16((B, H, Skv, D), seed + 1)
+    vb = inputs.random_bf16((B, H, Skv, D), seed + 2)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    if dtype == "f16":
+        q, k, v = (x.float().half() for x in (q, k, v))
+    od = torch.float32 if out_f32 else None
+    o_ref, l_ref = cp.attn_fwd_ex(q, k, v, out_dtype=od)
+    kt = k.transpose(2, 3).contiguous()
+    o, l = cp.attn_fwd_ex(q, kt, v, out_dtype=od, k_seq_last=True)
+    torch.cuda.synchronize()
+    assert same_bits(o, o_ref) and same_bits(l, l_ref)
+    if dtype == "bf16":
+        O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+        assert_bf16_parity(host64(o), host64(l), O, L, "K sequence-last")
+
+
+def test_k_seq_last_split_and_accumulate():
+    """The key-range split and the accumulate epilogue with K sequence-last: chunks of keys folded
+    into one f32 accumulator, each call with its planned workspace, equal the head-major fold bit
+    for bit and the oracle over all keys."""
+    B, H, Sq, D = 1, 2, 1000, 128
+    edges = [0, 1504, 1512, 3000]
+    qb = inputs.random_bf16((B, H, Sq, D), 4500)
+    kb = inputs.random_bf16((B, H, edges[-1], D), 4501)
+    vb = inputs.random_bf16((B, H, edges[-1], D), 4502)
+    q = dev_bf16(qb)
+    outs = {}
+    for kt_layout in (False, True):
+        o = torch.empty((B, H, Sq, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, H, Sq), device="cuda")
+        for i, (a, b) in enumerate(zip(edges[:-1], edges[1:])):
+            k = dev_bf16(np.ascontiguousarray(kb[:, :, a:b]))
+            v = dev_bf16(np.ascontiguousarray(vb[:, :, a:b]))
+            n = cp.attn_fwd_workspace_size(B, H, Sq, b - a, D, o_dtype=1)
+            ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+            if kt_layout:
+                k = k.transpose(2, 3).contiguous()
+            cp.attn_fwd_ex(q, k, v, o=o, lse=lse, workspace=ws, accumulate=i > 0, k_seq_last=kt_layout)
+        outs[kt_layout] = (o, lse)
+    torch.cuda.synchronize()
+    assert same_bits(outs[True][0], outs[False][0]) and same_bits(outs[True][1], outs[False][1])
+    O, L = oracle.attention(f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb), scale_of(D))
+    assert_bf16_parity(host64(outs[True][0]), host64(outs[True][1]), O, L, "K sequence-last folded")
+
+
+def test_k_seq_last_many_units():
+    """Enough tiles for the dynamic schedule's per-XCD ranges and its tail, and a split of the
+    last wave: K sequence-last equals K head-major bit for bit (outputs pre-filled with NaN)."""
+    B, H, Sq, Skv, D = 1, 24, 5520, 2992, 128
+    qb = inputs.random_bf16((B, H, Sq, D), 4600)
+    kb = inputs.random_bf16((B, H, Skv, D), 4601)
+    vb = inputs.random_bf16((B, H, Skv, D), 4602)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    n = cp.attn_fwd_workspace_size(B, H, Sq, Skv, D)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    o_ref, l_ref = cp.attn_fwd_ex(q, k, v, workspace=ws)
+    o = torch.full_like(o_ref, float("nan"))
+    l = torch.full_like(l_ref, float("nan"))
+    cp.attn_fwd_ex(q, k.transpose(2, 3).contiguous(), v, o=o, lse=l, workspace=ws, k_seq_last=True)
+    torch.cuda.synchronize()
+    assert same_bits(o, o_ref) and same_bits(l, l_ref)
