@@ -40,7 +40,10 @@
 // kv0 + L/4, columns d0 + 4(L%4) .. +3 and receives V[kv0 .. kv0+3][d0 + L],
 // i.e. four keys of one head-dim column -- exactly the per-lane k-slots above.
 // The swizzles make the K reads (16 rows x one chunk) and the V transposing
-// reads (4 rows x 4 chunks) hit 64 distinct banks.
+// reads (4 rows x 4 chunks) hit 64 distinct banks.  With K stored sequence-last
+// ([D, keys] per head) a K block is a [D][64] tile instead, and its fragments
+// come from two transposing reads each, which give every lane the same values
+// as the row-major tile.
 //
 // Schedule.  Per key block j a wave runs an MFMA slot M_j = {S_j = K_j Q^T,
 // O += V_{j-1} P_{j-1}} and a softmax slot SM_j (max, exp2, row sum, bf16
