@@ -326,21 +326,28 @@ __device__ __forceinline__ int attn_unit_fp8(int k_unit, const uint8_t* __restri
         // (the barrier orders memory only, and the max is already known before it)
         asm volatile("" : "+v"(m_run));
         const float mb = kPScaleLog2 - m_run;   // weights come out scaled by 2^7
-        // row sum in four independent partial sums (no serial chain of 32 dependent adds)
-        float psum[4] = {0.f, 0.f, 0.f, 0.f};
+        // Every exponent argument of the block first, then every exponential, then the row sum
+        // (four independent partial sums, no serial chain of dependent adds) and the packs, kept
+        // apart by scheduling fences so that no instruction waits on the one just before it.
+#pragma unroll
+        for (int x = 0; x < NKT * 16; ++x) s[x / 16][x % 16] = __builtin_fmaf(s[x / 16][x % 16], c, mb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < NKT * 16; ++x) s[x / 16][x % 16] = exp2_fast(s[x / 16][x % 16]);
+        __builtin_amdgcn_sched_barrier(0);
+        float psum[4];
+#pragma unroll
+        for (int x = 0; x < NKT * 16; ++x) {
+            if (x < 4) psum[x] = s[0][x];
+            else psum[x & 3] += s[x / 16][x % 16];
+        }
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    p[e] = exp2_fast(__builtin_fmaf(s[kt][w * 4 + e], c, mb));
-                    psum[e] += p[e];
-                }
                 // both halves of the word are written, so the previous contents are irrelevant
-                int word = pack_fp8x2<false>(p[0], p[1], pb[kt * 4 + w]);
-                word = pack_fp8x2<true>(p[2], p[3], word);
+                int word = pack_fp8x2<false>(s[kt][w * 4 + 0], s[kt][w * 4 + 1], pb[kt * 4 + w]);
+                word = pack_fp8x2<true>(s[kt][w * 4 + 2], s[kt][w * 4 + 3], word);
                 pb[kt * 4 + w] = word;
             }
         l_run = l_run * alpha + ((psum[0] + psum[1]) + (psum[2] + psum[3]));

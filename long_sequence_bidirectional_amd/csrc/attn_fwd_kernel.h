@@ -485,31 +485,43 @@ __device__ __forceinline__ int attn_unit(
                     if (key >= Skv) s[kt][i] = -INFINITY;
                 }
         }
-        float mx = s[0][0];
+        // Row max and row sum each in four independent partials (no serial chain of dependent
+        // instructions through the block).
+        float mxp[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+            for (int i = kt == 0 ? 4 : 0; i < 16; ++i) mxp[i & 3] = fmaxf(mxp[i & 3], s[kt][i]);
+        float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
         mx = max_across_halves(mx) * c;
         const bool raise = mx > m_run + kRescaleTh;
         const float m_new = raise ? mx : m_run;
         alpha = exp2_fast(m_run - m_new);   // 1 when not raised; 0 on the first block
         m_run = m_new;
-        float psum = 0.f;
+        // Every exponent argument of the block first, then every exponential, then the sums and
+        // packs: kept apart by scheduling fences, no instruction waits on the one just before it
+        // (measured 1.2-2% faster for the whole kernel than each weight's fma, exp2, add in turn).
+#pragma unroll
+        for (int x = 0; x < NKT * 16; ++x) s[x / 16][x % 16] = __builtin_fmaf(s[x / 16][x % 16], c, -m_new);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < NKT * 16; ++x) s[x / 16][x % 16] = exp2_fast(s[x / 16][x % 16]);
+        __builtin_amdgcn_sched_barrier(0);
+        float psum[4];
+#pragma unroll
+        for (int x = 0; x < NKT * 16; ++x) {
+            if (x < 4) psum[x] = s[0][x];
+            else psum[x & 3] += s[x / 16][x % 16];
+        }
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = exp2_fast(__builtin_fmaf(s[kt][half * 8 + e], c, -m_new));
-                    psum += p[e];
-                }
-                pb[kt * 2 + half] = u32x4{pack16x2<F16>(p[0], p[1]), pack16x2<F16>(p[2], p[3]),
-                                          pack16x2<F16>(p[4], p[5]), pack16x2<F16>(p[6], p[7])};
-            }
-        l_run = l_run * alpha + psum;
+            for (int half = 0; half < 2; ++half)
+                pb[kt * 2 + half] = u32x4{pack16x2<F16>(s[kt][half * 8 + 0], s[kt][half * 8 + 1]),
+                                          pack16x2<F16>(s[kt][half * 8 + 2], s[kt][half * 8 + 3]),
+                                          pack16x2<F16>(s[kt][half * 8 + 4], s[kt][half * 8 + 5]),
+                                          pack16x2<F16>(s[kt][half * 8 + 6], s[kt][half * 8 + 7])};
+        l_run = l_run * alpha + ((psum[0] + psum[1]) + (psum[2] + psum[3]));
         // keep the row sum and the packed weights materialised in this slot (otherwise
         // the compiler defers them past the barrier and holds every weight live)
         asm volatile("" : "+v"(l_run));
