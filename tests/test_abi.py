@@ -212,7 +212,7 @@ def test_counter_area_constant():
 def test_split_plan(L):
     """The planner's choices, worked out by hand for 256 resident workgroups (one per CU):
     T tiles of 256 rows leave T mod 256 tiles for the last wave; s pieces of those cost
-    ceil(rem*s/256) * (1/s + 4/nblk) tile-times against 1 for no split.  Every workspace
+    ceil(rem*s/256) * (1/s + 4/nblk) tile-times against 1 for no split, with s <= nblk / 8.  Every workspace
     starts with SCHED bytes of schedule counters; the pieces take the rest."""
     # video self-attention: 24 * 173 = 4152 tiles, 56 in the last wave, 690 key blocks.
     # One round: s = 4 (56 * 4 <= 256) costs 0.2558; two rounds of s = 9 (504 pieces)
@@ -222,16 +222,18 @@ def test_split_plan(L):
     assert plan(L, Sq=5520) == (16, 16, SCHED + 256 * piece_bytes(128))
     # Ulysses rank: 3 * 173 = 519 tiles, 7 left over -> 36 pieces (252 <= 256; 0.0336)
     assert plan(L, H=3) == (7, 36, SCHED + 252 * piece_bytes(128))
-    # ring chunk: 528 tiles against 87 key blocks: s <= 21 by the 4-block minimum; 16 (0.108)
-    assert plan(L, Sq=5520, Skv=5520) == (16, 16, SCHED + 256 * piece_bytes(128))
+    # ring chunk: 528 tiles against 87 key blocks: s <= 10 by the 8-block minimum; 10 (0.146)
+    assert plan(L, Sq=5520, Skv=5520) == (16, 10, SCHED + 160 * piece_bytes(128))
     # a full last wave: nothing to split (the counters are still used)
     assert plan(L, H=16, Sq=4096) == (0, 1, SCHED)
     # 250 of 256 slots busy in the last wave: splitting cannot beat one round
     assert plan(L, H=22, Sq=5888) == (0, 1, SCHED)
-    # fewer than 8 key blocks: never split
+    # fewer than 16 key blocks (two pieces of 8): never split
     assert plan(L, H=1, Sq=300, Skv=448) == (0, 1, SCHED)
-    # few tiles, few keys: 8 tiles, 47 blocks -> at most 11 pieces of >= 4 blocks
-    assert plan(L, H=2, Sq=1000, Skv=3000) == (8, 11, SCHED + 88 * piece_bytes(128))
+    assert plan(L, H=1, Sq=300, Skv=960) == (0, 1, SCHED)
+    assert plan(L, H=1, Sq=300, Skv=1024) == (2, 2, SCHED + 4 * piece_bytes(128))
+    # few tiles, few keys: 8 tiles, 47 blocks -> at most 5 pieces of >= 8 blocks
+    assert plan(L, H=2, Sq=1000, Skv=3000) == (8, 5, SCHED + 40 * piece_bytes(128))
     # the workspace bounds the pieces: room for 100 -> 6 per tile of 16
     assert plan(L, Sq=5520, ws=SCHED + 100 * piece_bytes(128) + 5) == (16, 6, SCHED + 96 * piece_bytes(128))
     # room for fewer than two pieces per tile, or no slots known: no split

@@ -71,10 +71,10 @@ def test_fp8_block_counts(Skv):
     check_fp8(q8, k8, v8, 1.0, 1.0, 1.0, 1.0 / math.sqrt(D), o, lse, f"fp8 Skv={Skv}")
 
 
-@pytest.mark.parametrize("Skv", [513, 577, 640, 704, 768])
+@pytest.mark.parametrize("Skv", [1025, 1089, 1152, 1216, 1280])
 def test_split_short_pieces(Skv):
-    """Few tiles (all in the device's last, partial wave) and 8-10 key blocks: the planner cuts
-    each tile into two or three pieces of four to five blocks, so every piece runs the shortest pipelines."""
+    """Few tiles (all in the device's last, partial wave) and 17-20 key blocks: the planner cuts
+    each tile into two pieces of eight to ten blocks, the shortest it makes."""
     B, H, Sq, D = 1, 2, 300, 128
     seed = 8300 + Skv
     qb = inputs.random_bf16((B, H, Sq, D), seed)

@@ -34,10 +34,10 @@ def same_bits(a, b):
 
 
 SPLIT_SHAPES = [
-    (1, 2, 1000, 3000, 128),   # 8 tiles (ragged last), 47 key blocks (56-key tail): 11 pieces per tile
-    (2, 3, 513, 700, 64),      # D = 64, 18 tiles, 11 blocks: 2 pieces
+    (1, 2, 1000, 3000, 128),   # 8 tiles (ragged last), 47 key blocks (56-key tail): 5 pieces per tile
+    (2, 3, 513, 1100, 64),     # D = 64, 18 tiles, 18 blocks (12-key tail): 2 pieces
     (1, 1, 17, 2992, 128),     # one tile of 17 rows, the text-token count (48-key tail)
-    (1, 3, 300, 600, 128),     # 10 blocks, 24-key tail
+    (1, 3, 300, 1080, 128),    # 17 blocks, 56-key tail: 2 pieces of 8 and 9 blocks
 ]
 
 
@@ -47,7 +47,9 @@ def test_split_full(B, H, Sq, Skv, D, out_f32):
     log(f"case: split B{B} H{H} Sq{Sq} Skv{Skv} D{D} out_f32={out_f32}")
     qb, kb, vb = rand_qkv(B, H, Sq, Skv, D, 3000 + Sq + Skv + D)
     ws, n = workspace(B, H, Sq, Skv, D, out_f32)
-    assert n > 0, "the planner was expected to split this shape"
+    tiles, pieces, _ = cp.attn_fwd_split_plan(B, H, Sq, Skv, D, 256, n)
+    log(f"  plan for 256 slots: {tiles} tiles x {pieces} pieces")
+    assert n > _lib.SCHED_BYTES, "the planner was expected to split this shape"
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     od = torch.float32 if out_f32 else None
     o, lse = cp.attn_fwd_ex(q, k, v, out_dtype=od, workspace=ws)
