@@ -391,8 +391,10 @@ def timed_leg(torch, stream, fn, flops=None, nbytes=None, iters=50, warmup=3, cl
     if nbytes is not None:
         out["GBps_median"] = round(nbytes / med / 1e6, 1)
     if clock:
+        # two readings in a row, the second kept: the first can still reflect the idle time
+        # before the leg (the board averages its power readings over a short window)
         sample = []
-        th = threading.Thread(target=lambda: sample.append(smi_sample()), daemon=True)
+        th = threading.Thread(target=lambda: (smi_sample(), sample.append(smi_sample())), daemon=True)
         th.start()
         while th.is_alive():      # keep this leg's kernel running until the reading is back
             for _ in range(4):
