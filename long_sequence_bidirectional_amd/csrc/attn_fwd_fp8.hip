@@ -505,15 +505,6 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
     __shared__ int next_unit;
     const int n_units = map.n_dp + map.n_split * map.split_s;
     const bool dynamic = map.sched != nullptr;
-    auto static_unit = [&](int64_t bid) -> int {
-        if (bid < map.grid_dp) {
-            const int u = (int)((bid % kNumXcd) * map.per_xcd_dp + bid / kNumXcd);
-            return u < map.n_dp ? u : -1;
-        }
-        const int64_t w = bid - map.grid_dp;
-        const int logical = (int)((w % kNumXcd) * map.per_xcd_sp + w / kNumXcd);
-        return logical < map.n_split * map.split_s ? map.n_dp + logical : -1;
-    };
     const int G = (int)gridDim.x;
     const int bb = (int)blockIdx.x;
     int64_t bid = bb;
@@ -522,7 +513,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
         u = sched_first(map, bb);
     } else {
         u = -1;
-        for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
+        for (; bid < n_grid && u < 0; bid += G) u = sched_static_unit(map, bid);
     }
     while (u >= 0 && u < n_units) {       // one call site: the unit body is inlined once
         const int claimed =
@@ -531,7 +522,7 @@ __global__ __launch_bounds__(512) void attn_fwd_fp8_kernel(const uint8_t* __rest
             u = claimed;
         } else {
             u = -1;
-            for (; bid < n_grid && u < 0; bid += G) u = static_unit(bid);
+            for (; bid < n_grid && u < 0; bid += G) u = sched_static_unit(map, bid);
         }
     }
 }
@@ -546,22 +537,14 @@ template <bool OUT_F32, bool SEQ>
 hipError_t launch_fp8_typed(const AttnFp8Args& a) {
     const int nQt = (int)((a.Sq + kBM - 1) / kBM);
     const int64_t total = a.BH * nQt;
-    AttnTileMap m{};
-    m.n_dp = (int)(total - a.split_tiles);
-    m.per_xcd_dp = (m.n_dp + kNumXcd - 1) / kNumXcd;
-    m.grid_dp = m.per_xcd_dp * kNumXcd;
-    m.n_split = (int)a.split_tiles;
-    m.split_s = a.split_tiles > 0 ? (int)a.split_pieces : 1;
-    m.per_xcd_sp = (m.n_split * m.split_s + kNumXcd - 1) / kNumXcd;
+    const UnitGrid ug = sched_plan(total, a.split_tiles, a.split_pieces, a.slots, a.sched != nullptr);
+    AttnTileMap m = ug.map;
     m.ws_o = a.ws_o;
     m.ws_lse = a.ws_lse;
     m.accumulate = a.accumulate ? 1 : 0;
     m.sched = a.sched;
-    const int grid = m.grid_dp + m.per_xcd_sp * kNumXcd;   // static unit grid (a multiple of kNumXcd)
+    const int grid = ug.grid, launch_grid = ug.launch_grid;
     const float c = (float)((double)a.scale * 1.4426950408889634 * (double)a.q_scale * (double)a.k_scale);
-    const int64_t cap = a.slots - a.slots % kNumXcd;
-    const int launch_grid = (cap > 0 && grid > cap) ? (int)cap : grid;
-    m.per_xcd = a.sched != nullptr ? sched_per_xcd(m.n_dp, launch_grid) : 0;
     if (a.sched != nullptr && a.sched_clear) {
         hipLaunchKernelGGL(zero_sched_kernel_fp8, dim3(1), dim3(256), 0, a.stream, a.sched_clear);
         const hipError_t ez = hipGetLastError();

@@ -1,4 +1,4 @@
-// The dynamic unit schedule of the persistent attention kernels.
+// The unit schedules of the persistent attention kernels.
 //
 // Units [0, n_units) are numbered as the kernels number them (whole query tiles in tile order,
 // then split pieces).  The first kNumXcd * per_xcd units (whole tiles only, in whole rounds of
@@ -10,9 +10,10 @@
 // under the power limit) take more of the tail.  Every ticket maps to a distinct unit and every
 // workgroup claims until it draws one past the end, so each unit runs exactly once.
 //
-// The mapping from tickets to units is plain arithmetic, written for host and device alike (a
-// CPU test drives it through random interleavings of the claims); only the counter increments
-// are device atomics.
+// The static order (no counters) and the unit map both launchers build are here too.  The
+// mapping from grid ids and tickets to units is plain arithmetic, written for host and device
+// alike (a CPU test drives it through random interleavings of the claims); only the counter
+// increments are device atomics.
 #pragma once
 
 #include <climits>
@@ -21,6 +22,46 @@
 #include "kernels.h"
 
 namespace cpattn {
+
+// Unit map of a launch over `total` query tiles whose last `split_tiles` are cut into `pieces`
+// key-range pieces each (unit numbering: whole tiles, then pieces piece-major), on at most
+// `slots` resident workgroups (0: unknown); `dynamic`: the counters are in use.  The static unit
+// grid `grid` holds each XCD's contiguous range of whole tiles and then of pieces, padded to a
+// multiple of the XCD count; the launch runs min(grid, slots rounded down to the XCD count)
+// persistent workgroups.  The launcher fills in the workspace, accumulate and counter fields.
+struct UnitGrid {
+    AttnTileMap map;
+    int grid;           // static unit grid ids [0, grid)
+    int launch_grid;    // workgroups launched
+};
+inline UnitGrid sched_plan(int64_t total, int64_t split_tiles, int64_t pieces, int64_t slots, bool dynamic) {
+    UnitGrid g{};
+    AttnTileMap& m = g.map;
+    m.n_dp = (int)(total - split_tiles);
+    m.per_xcd_dp = (m.n_dp + kNumXcd - 1) / kNumXcd;
+    m.grid_dp = m.per_xcd_dp * kNumXcd;
+    m.n_split = (int)split_tiles;
+    m.split_s = split_tiles > 0 ? (int)pieces : 1;
+    m.per_xcd_sp = (m.n_split * m.split_s + kNumXcd - 1) / kNumXcd;
+    g.grid = m.grid_dp + m.per_xcd_sp * kNumXcd;
+    const int64_t cap = slots - slots % kNumXcd;
+    g.launch_grid = (cap > 0 && g.grid > cap) ? (int)cap : g.grid;
+    m.per_xcd = dynamic ? sched_per_xcd(m.n_dp, g.launch_grid) : 0;
+    return g;
+}
+
+// Static schedule: the unit of static grid id `bid`, or -1 for the padding ids.  Ids are dealt
+// round-robin over the XCDs (workgroup b runs ids b, b + G, ...) and mapped so that each XCD walks
+// a contiguous range of whole tiles, then of pieces.
+__host__ __device__ __forceinline__ int sched_static_unit(const AttnTileMap& m, int64_t bid) {
+    if (bid < m.grid_dp) {
+        const int u = (int)((bid % kNumXcd) * m.per_xcd_dp + bid / kNumXcd);
+        return u < m.n_dp ? u : -1;
+    }
+    const int64_t w = bid - m.grid_dp;
+    const int logical = (int)((w % kNumXcd) * m.per_xcd_sp + w / kNumXcd);
+    return logical < m.n_split * m.split_s ? m.n_dp + logical : -1;
+}
 
 // First unit of workgroup b of a grid of G.
 __host__ __device__ __forceinline__ int sched_first(const AttnTileMap& m, int b) {

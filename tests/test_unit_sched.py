@@ -1,9 +1,10 @@
-"""CPU check of the attention kernels' dynamic unit schedule (csrc/unit_sched.h).
+"""CPU check of the attention kernels' unit schedules (csrc/unit_sched.h).
 
-The header's ticket-to-unit mapping is plain host/device arithmetic; `unit_sched_check.hip`
-builds it for the host only and simulates persistent workgroups claiming units in random
-interleavings, at the bench's shapes and at random unit counts (up to 4600 whole tiles plus split
-pieces) on 8 to 512 workgroups.  Every unit must run exactly once.  No GPU is used."""
+The header's unit map and its grid-id-to-unit and ticket-to-unit mappings are plain host/device
+arithmetic; `unit_sched_check.hip` builds them for the host only, walks the static order and
+simulates persistent workgroups claiming units in random interleavings, at the bench's shapes and
+at random tile counts (up to 4600 tiles, some split into pieces) on 8 to 512 resident workgroups
+(or an unknown count).  In both orders every unit must run exactly once.  No GPU is used."""
 import os
 import subprocess
 
