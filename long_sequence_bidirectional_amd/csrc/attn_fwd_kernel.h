@@ -756,7 +756,6 @@ __global__ __launch_bounds__(512) void attn_fwd_mfma_kernel(
     __shared__ int next_unit;
     const int n_units = map.n_dp + map.n_split * map.split_s;
     const bool dynamic = map.sched != nullptr;
-    // Unit of static grid id `bid`, or -1 for the padding ids of the XCD-aware map.
     const int G = (int)gridDim.x;
     const int b = (int)blockIdx.x;
     int64_t bid = b;                       // static schedule: next grid id (64-bit: no overflow near INT_MAX)
