@@ -136,7 +136,9 @@ __global__ __launch_bounds__(256) void attn_merge_wide_kernel(const void* o_a, c
 // where the partials are the tile's pieces (normalised f32 O, natural LSE) and,
 // when accumulating, the (O, LSE) already in o/lse.  One row per D/4 lanes, four
 // elements per lane.
-template <MergeOut T>
+// NP > 0: at most NP pieces, all read in one batch (the host picks the smallest instantiated NP
+// that holds the tile's pieces); NP = 0: any count, read in batches.
+template <MergeOut T, int NP>
 __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restrict__ ws_o,
                                                            const float* __restrict__ ws_lse, void* o, float* lse,
                                                            int first_tile, int n_split, int pieces, int nQt, int H,
@@ -156,47 +158,76 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const float* __restri
     const int64_t orow = (bh / H) * so.batch + (bh % H) * so.head + qrow * so.row;   // o offset
     const float* lp = ws_lse + (size_t)ti * pieces * TR + r;
     const float* op = ws_o + ((size_t)ti * pieces * TR + r) * D + c4;
-    // The pieces' values are read in batches of independent loads (indices clamped to the last
-    // piece, values past it ignored), so each batch costs one memory round trip rather than one
-    // per piece.
-    constexpr int LB = 16, OB = 8;
+    // With NP > 0 every piece's LSE and O and the old row are read in one batch of independent
+    // loads (indices clamped to the last piece, values past it ignored), so the merge costs one
+    // memory round trip; otherwise the pieces are read in batches.  Both paths fold in the same
+    // order, so they give the same bits.
     const float la = accumulate ? lse[row] : -INFINITY;
-    float mx = la;
-    for (int p0 = 0; p0 < pieces; p0 += LB) {
-        float l[LB];
-#pragma unroll
-        for (int i = 0; i < LB; ++i) l[i] = lp[(size_t)min(p0 + i, pieces - 1) * TR];
-#pragma unroll
-        for (int i = 0; i < LB; ++i)
-            if (p0 + i < pieces) mx = fmaxf(mx, l[i]);
-    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = -INFINITY;
-    if (mx != -INFINITY) {
-        float tot = expf(la - mx);
+    if constexpr (NP > 0) {
+        float l[NP];
+        f32x4 ov[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const size_t pc = (size_t)min(i, pieces - 1);
+            l[i] = lp[pc * TR];
+            ov[i] = *reinterpret_cast<const f32x4*>(op + pc * TR * D);
+        }
+        const f32x4 old = accumulate ? *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow + c4)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+        float mx = la;
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+            if (i < pieces) mx = fmaxf(mx, l[i]);
+        if (mx != -INFINITY) {
+            float tot = expf(la - mx);
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+                if (i < pieces) tot += expf(l[i] - mx);
+            L = mx + logf(tot);
+            if (accumulate) acc = old * expf(la - L);
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+                if (i < pieces) acc += ov[i] * expf(l[i] - L);
+        }
+    } else {
+        constexpr int LB = 16, OB = 8;
+        float mx = la;
         for (int p0 = 0; p0 < pieces; p0 += LB) {
             float l[LB];
 #pragma unroll
             for (int i = 0; i < LB; ++i) l[i] = lp[(size_t)min(p0 + i, pieces - 1) * TR];
 #pragma unroll
             for (int i = 0; i < LB; ++i)
-                if (p0 + i < pieces) tot += expf(l[i] - mx);
+                if (p0 + i < pieces) mx = fmaxf(mx, l[i]);
         }
-        L = mx + logf(tot);
-        if (accumulate) acc = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow + c4) *
-                              expf(la - L);
-        for (int p0 = 0; p0 < pieces; p0 += OB) {
-            f32x4 ov[OB];
-            float l[OB];
+        if (mx != -INFINITY) {
+            float tot = expf(la - mx);
+            for (int p0 = 0; p0 < pieces; p0 += LB) {
+                float l[LB];
 #pragma unroll
-            for (int i = 0; i < OB; ++i) {
-                const size_t pc = (size_t)min(p0 + i, pieces - 1);
-                ov[i] = *reinterpret_cast<const f32x4*>(op + pc * TR * D);
-                l[i] = lp[pc * TR];
+                for (int i = 0; i < LB; ++i) l[i] = lp[(size_t)min(p0 + i, pieces - 1) * TR];
+#pragma unroll
+                for (int i = 0; i < LB; ++i)
+                    if (p0 + i < pieces) tot += expf(l[i] - mx);
             }
+            L = mx + logf(tot);
+            if (accumulate) acc = *reinterpret_cast<const f32x4*>(static_cast<const float*>(o) + orow + c4) *
+                                  expf(la - L);
+            for (int p0 = 0; p0 < pieces; p0 += OB) {
+                f32x4 ov[OB];
+                float l[OB];
 #pragma unroll
-            for (int i = 0; i < OB; ++i)
-                if (p0 + i < pieces) acc += ov[i] * expf(l[i] - L);
+                for (int i = 0; i < OB; ++i) {
+                    const size_t pc = (size_t)min(p0 + i, pieces - 1);
+                    ov[i] = *reinterpret_cast<const f32x4*>(op + pc * TR * D);
+                    l[i] = lp[pc * TR];
+                }
+#pragma unroll
+                for (int i = 0; i < OB; ++i)
+                    if (p0 + i < pieces) acc += ov[i] * expf(l[i] - L);
+            }
         }
     }
     if constexpr (T == MergeOut::F32) {
@@ -247,11 +278,24 @@ hipError_t launch_attn_merge(const MergeArgs& a) {
     }
 }
 
+template <MergeOut T, int NP>
+void launch_pieces_np(const MergePiecesArgs& a, int64_t blocks) {
+    hipLaunchKernelGGL((merge_pieces_kernel<T, NP>), dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o, a.ws_lse,
+                       a.o, a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, (int)a.H, a.so, a.Sq, (int)a.D,
+                       a.accumulate ? 1 : 0);
+}
+
+// Piece counts read in one batch: the smallest of these that holds a tile's pieces (the planner's
+// usual counts lie between 4 and 36; more pieces take the batched path).
 template <MergeOut T>
 void launch_pieces_typed(const MergePiecesArgs& a, int64_t blocks) {
-    hipLaunchKernelGGL(merge_pieces_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, a.stream, a.ws_o, a.ws_lse, a.o,
-                       a.lse, a.first_tile, a.n_split, a.pieces, a.nQt, (int)a.H, a.so, a.Sq, (int)a.D,
-                       a.accumulate ? 1 : 0);
+    if (a.pieces <= 4) launch_pieces_np<T, 4>(a, blocks);
+    else if (a.pieces <= 8) launch_pieces_np<T, 8>(a, blocks);
+    else if (a.pieces <= 12) launch_pieces_np<T, 12>(a, blocks);
+    else if (a.pieces <= 16) launch_pieces_np<T, 16>(a, blocks);
+    else if (a.pieces <= 24) launch_pieces_np<T, 24>(a, blocks);
+    else if (a.pieces <= 36) launch_pieces_np<T, 36>(a, blocks);
+    else launch_pieces_np<T, 0>(a, blocks);
 }
 
 hipError_t launch_merge_pieces(const MergePiecesArgs& a) {
