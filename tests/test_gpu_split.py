@@ -209,3 +209,36 @@ def test_ring_driver_many_chunks(H, Sq):
     rows = np.array([0, 1, 255, 256, 1000, 2303, Sq - 1])
     O, L = oracle.attention_rows(f64_of_bf16(qb), f64_of_bf16(k_all), f64_of_bf16(v_all), scale_of(D), rows)
     assert_bf16_parity(host64(o[:, :, rows]), host64(l[:, :, rows]), O, L, "ring over 35 chunks")
+
+
+@pytest.mark.parametrize("s", [3, 7, 20, 48])
+def test_piece_merge_paths(s):
+    """The piece merge reads a tile's pieces in one batch for up to 36 pieces (instantiated for
+    4, 8, 12, 16, 24 and 36) and in batches beyond; the bench shapes use 4, 9, 10, 16 and 36
+    pieces.  Here 258 tiles of one head on 256 slots leave 2 split tiles, 384 key blocks allow up
+    to 48 pieces each, and the workspace size holds the plan to s pieces: 3, 7 and 20 take the
+    4-, 8- and 24-piece forms, 48 the batched path.  Both output types; the f32 call accumulates
+    onto the result of a separate key set, so the merge also folds in an existing row.  The split
+    tiles' rows and a sample of whole-tile rows are checked against the oracle."""
+    B, H, Sq, Skv, D = 1, 1, 258 * 256, 384 * 64, 128
+    piece = 256 * (D + 1) * 4
+    nbytes = _lib.SCHED_BYTES + 2 * s * piece
+    tiles, pieces, used = cp.attn_fwd_split_plan(B, H, Sq, Skv, D, 256, nbytes)
+    log(f"case: piece merge, {tiles} split tiles x {pieces} pieces (workspace {nbytes} B)")
+    assert (tiles, pieces) == (2, s)
+    qb, kb, vb = rand_qkv(B, H, Sq, Skv, D, 3400 + s)
+    ka, va = inputs.random_bf16((B, H, 512, D), 3460 + s), inputs.random_bf16((B, H, 512, D), 3470 + s)
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o16, l16 = cp.attn_fwd_ex(q, k, v, workspace=ws)
+    o32, l32 = cp.attn_fwd(q, dev_bf16(ka), dev_bf16(va), out_dtype=torch.float32)
+    cp.attn_fwd_ex(q, k, v, o=o32, lse=l32, workspace=ws, accumulate=True)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(256 * 256, Sq), inputs.sample_rows(256 * 256, 32, seed=3480 + s)])
+    q64, k64, v64 = f64_of_bf16(qb), f64_of_bf16(kb), f64_of_bf16(vb)
+    O, L = oracle.attention_rows(q64, k64, v64, scale_of(D), rows)
+    assert_bf16_parity(host64(o16[:, :, rows]), host64(l16[:, :, rows]), O, L, f"{s} pieces, bf16 O")
+    kc = np.concatenate([f64_of_bf16(ka), k64], axis=2)
+    vc = np.concatenate([f64_of_bf16(va), v64], axis=2)
+    O, L = oracle.attention_rows(q64, kc, vc, scale_of(D), rows)
+    assert_bf16_parity(host64(o32[:, :, rows]), host64(l32[:, :, rows]), O, L, f"{s} pieces, f32 O accumulated")
