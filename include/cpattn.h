@@ -1,6 +1,6 @@
 /*
  * cpattn -- per-rank attention for context-parallel diffusion transformers
- * on AMD Instinct MI355X (gfx950).  C ABI, version 3.
+ * on AMD Instinct MI355X (gfx950).  C ABI, version 4 (CPATTN_ABI_VERSION).
  *
  * What the library computes (sources are the pages' titles and sections):
  *
@@ -57,6 +57,10 @@
  *    holds at once and of that array's device address.
  *  - Work is enqueued on the caller's HIP stream (0 = the null stream) and
  *    runs asynchronously; the call returns once the launches are enqueued.
+ *    A call enqueues kernels only (no memset, copy, allocation or
+ *    synchronisation), so calls can be recorded into a HIP graph by stream
+ *    capture; make one call on the device before capturing, so that the
+ *    one-time per-device lookups described below run outside the capture.
  *  - Argument checks run synchronously, on the host, before any HIP call.
  *    A failed check returns its status and enqueues nothing.  A launch
  *    failure returns CPATTN_E_HIP.  Faults inside a kernel surface at the
