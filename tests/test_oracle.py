@@ -213,7 +213,10 @@ def test_unmutated_copy_passes_pins():
 
 
 # ----------------------------------------------------------------------- merge
-def test_merge_equals_unchunked():
+# The merge pins take the merge function as an argument, so that the planted-mistake
+# test below can run them against deliberately wrong merges.
+def merge_pin_chunked(merge):
+    """Attention over all keys equals the merge of attention over disjoint chunks."""
     B, H, Sq, D = 1, 2, 20, 8
     q = rnd((B, H, Sq, D), 70)
     k, v = rnd((B, H, 57, D), 71), rnd((B, H, 57, D), 72)
@@ -222,40 +225,102 @@ def test_merge_equals_unchunked():
     # two chunks, then eight uneven chunks folded left to right
     Oa, La = oracle.attention(q, k[:, :, :20], v[:, :, :20], s)
     Ob, Lb = oracle.attention(q, k[:, :, 20:], v[:, :, 20:], s)
-    Om, Lm = oracle.merge(Oa, La, Ob, Lb)
+    Om, Lm = merge(Oa, La, Ob, Lb)
     np.testing.assert_allclose(Om, O, rtol=0, atol=TOL)
     np.testing.assert_allclose(Lm, L, rtol=0, atol=TOL)
     edges = [0, 3, 10, 11, 30, 31, 44, 50, 57]
     acc = (np.zeros_like(O), np.full(L.shape, -np.inf))
     for a, b in zip(edges[:-1], edges[1:]):
         Oc, Lc = oracle.attention(q, k[:, :, a:b], v[:, :, a:b], s)
-        acc = oracle.merge(acc[0], acc[1], Oc, Lc)
+        acc = merge(acc[0], acc[1], Oc, Lc)
     np.testing.assert_allclose(acc[0], O, rtol=0, atol=TOL)
     np.testing.assert_allclose(acc[1], L, rtol=0, atol=TOL)
 
 
-def test_merge_algebra():
+def merge_pin_algebra(merge):
+    """Identity, commutativity, associativity, two empty sides, equal LSEs."""
     o1, l1 = rnd((2, 5, 4), 80), rnd((2, 5), 81) * 3
     o2, l2 = rnd((2, 5, 4), 82), rnd((2, 5), 83) * 3
     o3, l3 = rnd((2, 5, 4), 84), rnd((2, 5), 85) * 3
     zero, ninf = np.zeros_like(o1), np.full(l1.shape, -np.inf)
-    oi, li = oracle.merge(o1, l1, zero, ninf)                 # identity
+    oi, li = merge(o1, l1, zero, ninf)                 # identity
     np.testing.assert_array_equal(oi, o1)
     np.testing.assert_array_equal(li, l1)
-    oa, la = oracle.merge(o1, l1, o2, l2)                     # commutativity
-    ob, lb = oracle.merge(o2, l2, o1, l1)
+    oa, la = merge(o1, l1, o2, l2)                     # commutativity
+    ob, lb = merge(o2, l2, o1, l1)
     np.testing.assert_allclose(oa, ob, rtol=0, atol=TOL)
     np.testing.assert_allclose(la, lb, rtol=0, atol=TOL)
-    x = oracle.merge(*oracle.merge(o1, l1, o2, l2), o3, l3)   # associativity
-    y = oracle.merge(o1, l1, *oracle.merge(o2, l2, o3, l3))
+    x = merge(*merge(o1, l1, o2, l2), o3, l3)          # associativity
+    y = merge(o1, l1, *merge(o2, l2, o3, l3))
     np.testing.assert_allclose(x[0], y[0], rtol=0, atol=TOL)
     np.testing.assert_allclose(x[1], y[1], rtol=0, atol=TOL)
-    oe, le = oracle.merge(zero, ninf, zero, ninf)             # both empty
+    oe, le = merge(zero, ninf, zero, ninf)             # both empty
     assert np.all(oe == 0) and np.all(np.isneginf(le))
     # equal LSE: weights one half each, LSE + ln 2
-    om, lm = oracle.merge(o1, l1, o2, l1)
+    om, lm = merge(o1, l1, o2, l1)
     np.testing.assert_allclose(om, 0.5 * (o1 + o2), rtol=0, atol=TOL)
     np.testing.assert_allclose(lm, l1 + math.log(2), rtol=0, atol=TOL)
+
+
+MERGE_PINS = [merge_pin_chunked, merge_pin_algebra]
+
+
+def test_merge_equals_unchunked():
+    merge_pin_chunked(oracle.merge)
+
+
+def test_merge_algebra():
+    merge_pin_algebra(oracle.merge)
+
+
+def _merge_mutant(kind):
+    """An independent row-by-row merge with one planted mistake (kind "none": no mistake)."""
+    def merge(o_a, lse_a, o_b, lse_b):
+        o_a, o_b = np.asarray(o_a, float), np.asarray(o_b, float)
+        la, lb = np.asarray(lse_a, float), np.asarray(lse_b, float)
+        o = np.zeros_like(o_a)
+        lse = np.full(la.shape, -np.inf)
+        for idx in np.ndindex(la.shape):
+            a, b = la[idx], lb[idx]
+            m = max(a, b)
+            if m == -np.inf and kind != "empty_gives_nan":
+                continue                                   # two empty sides: O = 0, LSE = -inf
+            with np.errstate(invalid="ignore"):
+                ea, eb = math.exp(a - m) if a > -np.inf else 0.0, math.exp(b - m) if b > -np.inf else 0.0
+                if kind == "empty_gives_nan" and m == -np.inf:
+                    ea = eb = float("nan")
+            tot = ea + eb
+            if kind == "lse_drops_max":
+                lse[idx] = math.log(tot)
+            elif kind == "lse_max_only":
+                lse[idx] = m
+            else:
+                lse[idx] = m + math.log(tot) if tot == tot else float("nan")
+            wa, wb = (ea, eb) if kind == "unnormalised_weights" else (ea / tot, eb / tot)
+            if kind == "swapped_weights":
+                wa, wb = wb, wa
+            o[idx] = wa * o_a[idx] + wb * o_b[idx]
+        return o, lse
+    return merge
+
+
+@pytest.mark.parametrize("kind", ["unnormalised_weights", "lse_drops_max", "lse_max_only", "swapped_weights",
+                                  "empty_gives_nan"])
+def test_merge_pins_catch_planted_mistakes(kind):
+    mutant = _merge_mutant(kind)
+    failures = 0
+    for pin in MERGE_PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            failures += 1
+    assert failures > 0, f"no merge pin caught the planted mistake {kind!r}"
+
+
+def test_merge_mutation_harness_faithful():
+    good = _merge_mutant("none")
+    for pin in MERGE_PINS:
+        pin(good)
 
 
 # -------------------------------------------------------------------- relayout
