@@ -48,7 +48,10 @@
  * Conventions shared by every entry point:
  *
  *  - Every tensor pointer is DEVICE memory owned by the caller, contiguous
- *    (row-major, last dimension fastest) and 16-byte aligned.  The library
+ *    (row-major, last dimension fastest) and 16-byte aligned.  A call's
+ *    buffers and stream belong to one device, which must be the calling
+ *    thread's current HIP device (the per-device state below is kept for the
+ *    current device).  The library
  *    never allocates, frees or retains caller memory and has no handles;
  *    scratch memory, where a call can use it, is a caller-owned workspace
  *    argument, except for cpattn_attn_fwd_ex_static, which uses a fixed
@@ -273,7 +276,8 @@ cpattn_status cpattn_attn_fwd_fp8(const void* q, const void* k, const void* v, v
 /*
  * Workspace bytes cpattn_attn_fwd_ex (in_dtype BF16 or F16) or cpattn_attn_fwd_fp8
  * (in_dtype E4M3, o_dtype BF16 or F32, D = 128) uses for this problem on the CURRENT
- * device (256 for the work counter when no split helps; 0 for f32 inputs).  Makes HIP queries of
+ * device (CPATTN_WORKSPACE_COUNTER_BYTES for the work counters when no split helps;
+ * 0 for f32 inputs).  Makes HIP queries of
  * the current device (CU count, kernel occupancy); CPATTN_E_HIP if they fail.
  * Shape checks as for cpattn_attn_fwd (the scale is not needed).
  */

@@ -61,10 +61,17 @@ def _dev(t, name, device=None):
     return t.data_ptr()
 
 
-def _stream(stream):
+def _launch(fn, device, *args, stream=None):
+    """Call C entry point `fn` with `args` and the stream, with the tensors' device current (the
+    library's per-device lookups use the current device).  The stream defaults to that device's
+    current stream; a stream given must belong to that device."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    if s.device != device:
+        raise ValueError(f"stream is on {s.device}, the tensors on {device}")
+    with torch.cuda.device(device):
+        st = getattr(lib(), fn)(*args, s.cuda_stream)
+    check(fn, st)
 
 
 def _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major=False, k_seq_last=False):
@@ -98,13 +105,13 @@ def _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major=False, k_seq_las
     dv = q.device
     args = (_dev(q, "q"), _dev(k, "k", dv) if Skv else None, _dev(v, "v", dv) if Skv else None,
             _dev(o, "o", dv), _dev(lse, "lse", dv), B, H, Sq, Skv, D, float(scale), _dtype_code(q), _dtype_code(o))
-    return o, lse, args
+    return o, lse, args, dv
 
 
 def attn_fwd(q, k, v, o=None, lse=None, scale=None, out_dtype=None, stream=None):
     """Non-causal attention with per-row LSE.  q [B,H,Sq,D], k/v [B,H,Skv,D]."""
-    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype)
-    check("cpattn_attn_fwd", lib().cpattn_attn_fwd(*args, _stream(stream)))
+    o, lse, args, dv = _attn_operands(q, k, v, o, lse, scale, out_dtype)
+    _launch("cpattn_attn_fwd", dv, *args, stream=stream)
     return o, lse
 
 
@@ -116,13 +123,13 @@ def attn_fwd_ex(q, k, v, o=None, lse=None, scale=None, out_dtype=None, workspace
     (k_seq_last: k [B,H,D,Skv] with head-major q, v, o; Skv a multiple of 8)."""
     if accumulate and (o is None or lse is None):
         raise ValueError("accumulate needs the existing o and lse")
-    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major, k_seq_last)
+    o, lse, args, dv = _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major, k_seq_last)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None and workspace.numel() > 0:
-        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+        ws_ptr, ws_bytes = _dev(workspace, "workspace", dv), workspace.numel() * workspace.element_size()
     flags = ((FLAG_ACCUMULATE if accumulate else 0) | (FLAG_SEQ_MAJOR if seq_major else 0)
              | (FLAG_K_SEQ_LAST if k_seq_last else 0))
-    check("cpattn_attn_fwd_ex", lib().cpattn_attn_fwd_ex(*args, flags, ws_ptr, ws_bytes, _stream(stream)))
+    _launch("cpattn_attn_fwd_ex", dv, *args, flags, ws_ptr, ws_bytes, stream=stream)
     return o, lse
 
 
@@ -134,13 +141,14 @@ def attn_fwd_ex_static(q, k, v, o=None, lse=None, scale=None, out_dtype=None, sc
     at most STATIC_SCRATCH_BYTES)."""
     if accumulate and (o is None or lse is None):
         raise ValueError("accumulate needs the existing o and lse")
-    o, lse, args = _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major)
+    o, lse, args, dv = _attn_operands(q, k, v, o, lse, scale, out_dtype, seq_major)
     if scratch_bytes is None:
         B, H, Sq, Skv, D = args[5], args[6], args[7], args[8], args[9]
-        scratch_bytes = min(attn_fwd_workspace_size(B, H, Sq, Skv, D, args[11], args[12]), STATIC_SCRATCH_BYTES)
+        with _torch().cuda.device(dv):
+            scratch_bytes = min(attn_fwd_workspace_size(B, H, Sq, Skv, D, args[11], args[12]),
+                                STATIC_SCRATCH_BYTES)
     flags = (FLAG_ACCUMULATE if accumulate else 0) | (FLAG_SEQ_MAJOR if seq_major else 0)
-    check("cpattn_attn_fwd_ex_static",
-          lib().cpattn_attn_fwd_ex_static(*args, flags, int(scratch_bytes), _stream(stream)))
+    _launch("cpattn_attn_fwd_ex_static", dv, *args, flags, int(scratch_bytes), stream=stream)
     return o, lse
 
 
@@ -166,25 +174,23 @@ def attn_fwd_fp8(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, o=None, lse=Non
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if accumulate and (o is None or lse is None):
+        raise ValueError("accumulate needs the existing o and lse")
     if o is None:
         o = torch.empty(o_shape, dtype=out_dtype or torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if tuple(o.shape) != o_shape or lse.shape != (B, H, Sq) or lse.dtype != torch.float32:
         raise ValueError(f"o must be {o_shape} and lse float32 [B,H,Sq]")
-    if accumulate and (o is None or lse is None):
-        raise ValueError("accumulate needs the existing o and lse")
     flags = (FLAG_SEQ_MAJOR if seq_major else 0) | (FLAG_ACCUMULATE if accumulate else 0)
     dv = q.device
     ws_ptr, ws_bytes = None, 0
     if workspace is not None and workspace.numel() > 0:
         ws_ptr, ws_bytes = _dev(workspace, "workspace", dv), workspace.numel() * workspace.element_size()
-    st = lib().cpattn_attn_fwd_fp8(_dev(q, "q"), _dev(k, "k", dv) if Skv else None,
-                                   _dev(v, "v", dv) if Skv else None, _dev(o, "o", dv), _dev(lse, "lse", dv),
-                                   B, H, Sq, Skv, D, float(scale), float(q_scale),
-                                   float(k_scale), float(v_scale), _dtype_code(o), flags, ws_ptr, ws_bytes,
-                                   _stream(stream))
-    check("cpattn_attn_fwd_fp8", st)
+    _launch("cpattn_attn_fwd_fp8", dv, _dev(q, "q"), _dev(k, "k", dv) if Skv else None,
+            _dev(v, "v", dv) if Skv else None, _dev(o, "o", dv), _dev(lse, "lse", dv),
+            B, H, Sq, Skv, D, float(scale), float(q_scale), float(k_scale), float(v_scale), _dtype_code(o), flags,
+            ws_ptr, ws_bytes, stream=stream)
     return o, lse
 
 
@@ -222,10 +228,10 @@ def attn_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
     for t in (lse_a, lse_b, lse_out):
         if t.dtype != torch.float32:
             raise TypeError("lse tensors must be float32")
-    st = lib().cpattn_attn_merge(_dev(o_a, "o_a"), _dev(lse_a, "lse_a"), _dev(o_b, "o_b"), _dev(lse_b, "lse_b"),
-                                 _dev(o_out, "o_out"), _dev(lse_out, "lse_out"), B, H, S, D,
-                                 _dtype_code(o_a), _stream(stream))
-    check("cpattn_attn_merge", st)
+    dv = o_a.device
+    _launch("cpattn_attn_merge", dv, _dev(o_a, "o_a"), _dev(lse_a, "lse_a", dv), _dev(o_b, "o_b", dv),
+            _dev(lse_b, "lse_b", dv), _dev(o_out, "o_out", dv), _dev(lse_out, "lse_out", dv), B, H, S, D,
+            _dtype_code(o_a), stream=stream)
     return o_out, lse_out
 
 
@@ -248,13 +254,11 @@ def ring_attn_fwd(q, k_chunks, v_chunks, o=None, lse=None, o_work=None, lse_work
         raise ValueError("give both o_work and lse_work, or neither")
     if o_work is None and use_work:   # scratch for the key-range split of partial waves
         o_work, lse_work = torch.empty_like(o), torch.empty_like(lse)
-    st = lib().cpattn_ring_attn_fwd(_dev(q, "q"), _dev(k_chunks, "k_chunks", dev) if Skv_c else None,
-                                    _dev(v_chunks, "v_chunks", dev) if Skv_c else None, _dev(o, "o", dev),
-                                    _dev(lse, "lse", dev),
-                                    _dev(o_work, "o_work", dev) if o_work is not None else None,
-                                    _dev(lse_work, "lse_work", dev) if lse_work is not None else None,
-                                    B, H, Sq, Skv_c, n, D, float(scale), _stream(stream))
-    check("cpattn_ring_attn_fwd", st)
+    _launch("cpattn_ring_attn_fwd", dev, _dev(q, "q"), _dev(k_chunks, "k_chunks", dev) if Skv_c else None,
+            _dev(v_chunks, "v_chunks", dev) if Skv_c else None, _dev(o, "o", dev), _dev(lse, "lse", dev),
+            _dev(o_work, "o_work", dev) if o_work is not None else None,
+            _dev(lse_work, "lse_work", dev) if lse_work is not None else None,
+            B, H, Sq, Skv_c, n, D, float(scale), stream=stream)
     return o, lse
 
 
@@ -269,9 +273,9 @@ def qk_rmsnorm(x, w, eps=1e-6, post_scale=1.0, out=None, stream=None):
     if out.shape != x.shape or out.dtype != x.dtype:
         raise ValueError("out must match x")
     rows = x.numel() // D
-    st = lib().cpattn_qk_rmsnorm(_dev(x, "x"), _dev(w, "w"), _dev(out, "out"), rows, D, float(eps),
-                                 float(post_scale), _dtype_code(x), _stream(stream))
-    check("cpattn_qk_rmsnorm", st)
+    dv = x.device
+    _launch("cpattn_qk_rmsnorm", dv, _dev(x, "x"), _dev(w, "w", dv), _dev(out, "out", dv), rows, D, float(eps),
+            float(post_scale), _dtype_code(x), stream=stream)
     return out
 
 
@@ -306,9 +310,9 @@ def _relayout(fn, src, P, direction, dst, pack, stream):
         dst = torch.empty(out_shape, dtype=src.dtype, device=src.device)
     if tuple(dst.shape) != tuple(out_shape) or dst.dtype != src.dtype:
         raise ValueError(f"dst must be {out_shape} of {src.dtype}")
-    st = getattr(lib(), fn)(_dev(src, "src"), _dev(dst, "dst"), B, S_l, H, D, P, _dtype_code(src), direction,
-                            _stream(stream))
-    check(fn, st)
+    dv = src.device
+    _launch(fn, dv, _dev(src, "src"), _dev(dst, "dst", dv), B, S_l, H, D, P, _dtype_code(src), direction,
+            stream=stream)
     return dst
 
 
@@ -343,11 +347,10 @@ def _relayout_n(fn, srcs, P, direction, dsts, pack, stream):
         if tuple(t.shape) != tuple(out_shape) or t.dtype != srcs[0].dtype:
             raise ValueError(f"every dst must be {out_shape} of {srcs[0].dtype}")
     n = len(srcs)
-    src_ptrs = (ctypes.c_void_p * n)(*(_dev(t, f"srcs[{i}]") for i, t in enumerate(srcs)))
-    dst_ptrs = (ctypes.c_void_p * n)(*(_dev(t, f"dsts[{i}]") for i, t in enumerate(dsts)))
-    st = getattr(lib(), fn)(src_ptrs, dst_ptrs, n, B, S_l, H, D, P, _dtype_code(srcs[0]), direction,
-                            _stream(stream))
-    check(fn, st)
+    dv = srcs[0].device
+    src_ptrs = (ctypes.c_void_p * n)(*(_dev(t, f"srcs[{i}]", dv) for i, t in enumerate(srcs)))
+    dst_ptrs = (ctypes.c_void_p * n)(*(_dev(t, f"dsts[{i}]", dv) for i, t in enumerate(dsts)))
+    _launch(fn, dv, src_ptrs, dst_ptrs, n, B, S_l, H, D, P, _dtype_code(srcs[0]), direction, stream=stream)
     return dsts
 
 

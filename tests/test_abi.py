@@ -170,6 +170,23 @@ def test_binding_k_seq_last_shapes():
         cp.attn_fwd_ex(q, torch.zeros((1, 2, 64, 24), dtype=torch.bfloat16), v, seq_major=True, k_seq_last=True)
 
 
+def test_binding_accumulate_needs_outputs():
+    """Accumulating folds into the (o, lse) already there, so every binding that accumulates
+    refuses a call without them before it allocates or touches a device (the fp8 binding once
+    allocated fresh outputs first, which made its check dead)."""
+    import torch
+    import long_sequence_bidirectional_amd as cp
+    q = torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 2, 24, 128), dtype=torch.bfloat16)
+    q8, kv8 = q.to(torch.uint8), kv.to(torch.uint8)
+    for fn, args in ((cp.attn_fwd_ex, (q, kv, kv)), (cp.attn_fwd_ex_static, (q, kv, kv)),
+                     (cp.attn_fwd_fp8, (q8, kv8, kv8))):
+        with pytest.raises(ValueError, match="accumulate needs"):
+            fn(*args, accumulate=True)
+        with pytest.raises(ValueError, match="accumulate needs"):
+            fn(*args, lse=torch.zeros((1, 2, 16)), accumulate=True)
+
+
 def test_attn_fwd_ex_static_validation(L):
     """Every check of attn_fwd_ex except the workspace pointer's, plus the scratch limit; all of
     them run before the one HIP call (the lookup of the scratch's device address)."""
