@@ -41,14 +41,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_video_layer_traffic
 CALIB_SHAPE = (1, 44160, 24, 128)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank lines (the compiled code does not depend on them).
+    The kernel sources hold no string literal with "//" or "/*" in it."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 over the sources of the bf16 attention kernel (template, instantiation, unit
-    schedule and the shared headers)."""
+    """SHA-256 over the code of the bf16 attention kernel's sources (template, instantiation, unit
+    schedule and the shared headers), comments left out."""
     import hashlib
     h = hashlib.sha256()
     for path in KERNEL_SRC:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 

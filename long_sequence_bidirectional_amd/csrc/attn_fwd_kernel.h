@@ -74,11 +74,12 @@
 //
 // Softmax in base 2: t = s * scale * log2(e), p = exp2(t - m), natural
 // LSE = (m + log2 l) * ln 2.  The running max m is only raised when a block's
-// max exceeds it by more than 2^8 (so p <= 256); otherwise the stale m is kept
-// and O needs no rescale.  The result is exact after the final division by l
-// because every term of O and l carries the same factor 2^-m.  Keys past Skv
-// in the last block get -inf.  Out-of-range rows are loaded clamped to the
-// last valid row (finite values that get weight 0 or are never stored).
+// max exceeds it by more than 8 (base-2 units, a factor of 2^8, so p <= 256);
+// otherwise the stale m is kept and O needs no rescale.  The result is exact
+// after the final division by l because every term of O and l carries the same
+// factor 2^-m.  Keys past Skv in the last block get -inf.  A lane whose query
+// row lies past Sq loads row Sq - 1 instead, so it computes that row's result
+// and stores the same bits there again.
 #pragma once
 
 #include <climits>
